@@ -1,0 +1,140 @@
+"""CPU oracle for compressed-attention block selection -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never loads it, and the
+two share no code: the oracle is the plain C definition in
+``ds_sel_oracle.c`` (admitted list -> fp32 scores in a fixed order -> qsort by
+(score desc, block asc) -> first min(k, admitted)), compiled with gcc into
+``libds_sel_oracle.so`` and driven through ctypes from here.
+
+What it follows: page "DeepSeek V4.1F Q4 on M3 Ultra with native DSpark MTP
+(40tps / 800tps)", paragraph "Decode at depth" (512 blocks per layer out of the
+whole context, only mask-admitted blocks are candidates, the admitted index is
+built per row, the top 512 are kept).  The score formula, the order and the
+padding are readings of this library, stated in the C file's header.
+
+Every array is host numpy; bf16 values travel as their uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "ds_sel_oracle.c")
+LIBRARY = os.path.join(_HERE, "libds_sel_oracle.so")
+
+# Flags that keep every fp32 operation a separately rounded IEEE operation.
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
+
+_lib = None
+
+
+def build(output: str = LIBRARY, source: str = SOURCE, extra_flags=()) -> str:
+    """Compile the C oracle with gcc into ``output`` (always recompiles)."""
+    tmp = output + ".tmp"
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-o", tmp, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, output)
+    return output
+
+
+def _declare(lib):
+    i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.ds_sel_oracle_select.restype = ctypes.c_int
+    lib.ds_sel_oracle_select.argtypes = [i32, i32, i32, i32, i64, i32, p, p, p, i64, i64, p, i64,
+                                         i64, p, p, p, p]
+    lib.ds_sel_oracle_score_blocks.restype = ctypes.c_int
+    lib.ds_sel_oracle_score_blocks.argtypes = [i32, i32, i32, i32, i64, p, p, p, i64, i64, i32,
+                                               i32, i64, p, p]
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle (building it first if it is missing)."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        _lib = _declare(ctypes.CDLL(LIBRARY))
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _shapes(q, w, keys, mask):
+    if q.ndim != 4:
+        raise ValueError("q must be [layers][rows][heads][dim]")
+    layers, rows, heads, dim = q.shape
+    if w.shape != (layers, rows, heads):
+        raise ValueError("w must be [layers][rows][heads]")
+    if keys.ndim != 3 or keys.shape[0] != layers or keys.shape[2] < dim:
+        raise ValueError("keys must be [layers][blocks][ldk] with ldk >= dim")
+    blocks, ldk = keys.shape[1], keys.shape[2]
+    mrow = mlayer = 0
+    if mask is not None:
+        if mask.ndim != 3 or mask.shape[0] != layers or mask.shape[1] not in (1, rows):
+            raise ValueError("mask must be [layers][rows or 1][words]")
+        if mask.shape[2] * 32 < blocks:
+            raise ValueError("mask rows need ceil(blocks/32) words")
+        mrow = 0 if mask.shape[1] == 1 else mask.shape[2]
+        mlayer = mask.shape[1] * mask.shape[2]
+    return layers, rows, heads, dim, blocks, ldk, mrow, mlayer
+
+
+def select(q, w, keys, k, mask=None, limit=None, lib=None):
+    """Top-k selection for every (layer, row).
+
+    q     uint16 [L][R][H][d]   bf16 bits
+    w     uint16 [L][R][H]      bf16 bits
+    keys  uint16 [L][N][ldk]    bf16 bits (ldk >= d; columns past d unused)
+    mask  uint32 [L][R or 1][words] or None (one shared row when the middle
+          dimension is 1)
+    limit int32 [L][R] or None
+    Returns (idx int32 [L][R][k], score float32 [L][R][k], count int32 [L][R]).
+    """
+    q, w, keys = _c(q, np.uint16), _c(w, np.uint16), _c(keys, np.uint16)
+    mask, limit = _c(mask, np.uint32), _c(limit, np.int32)
+    layers, rows, heads, dim, blocks, ldk, mrow, mlayer = _shapes(q, w, keys, mask)
+    if limit is not None and limit.shape != (layers, rows):
+        raise ValueError("limit must be [layers][rows]")
+    idx = np.empty((layers, rows, k), np.int32)
+    score = np.empty((layers, rows, k), np.float32)
+    count = np.empty((layers, rows), np.int32)
+    lib = lib or load()
+    rc = lib.ds_sel_oracle_select(layers, rows, heads, dim, blocks, k, _ptr(q), _ptr(w),
+                                  _ptr(keys), ldk, blocks * ldk, _ptr(mask), mrow, mlayer,
+                                  _ptr(limit), _ptr(idx), _ptr(score), _ptr(count))
+    if rc != 0:
+        raise OracleError(f"ds_sel_oracle_select returned {rc}")
+    return idx, score, count
+
+
+def score_blocks(q, w, keys, layer, row, blocks_list, lib=None):
+    """fp32 scores (the oracle's fixed order) of the listed blocks of one (layer, row)."""
+    q, w, keys = _c(q, np.uint16), _c(w, np.uint16), _c(keys, np.uint16)
+    lst = _c(blocks_list, np.int32)
+    layers, rows, heads, dim, blocks, ldk, _, _ = _shapes(q, w, keys, None)
+    out = np.empty(lst.shape[0], np.float32)
+    lib = lib or load()
+    rc = lib.ds_sel_oracle_score_blocks(layers, rows, heads, dim, blocks, _ptr(q), _ptr(w),
+                                        _ptr(keys), ldk, blocks * ldk, layer, row, lst.shape[0],
+                                        _ptr(lst), _ptr(out))
+    if rc != 0:
+        raise OracleError(f"ds_sel_oracle_score_blocks returned {rc}")
+    return out

@@ -1,0 +1,264 @@
+"""Independent pins for the CPU oracle.
+
+Nothing here reuses the oracle's code.  The checks rest on:
+  * exact integer arithmetic: on inputs whose bf16 values are small integers
+    every fp32 partial sum is an integer below 2**24, so the oracle's fp32
+    score must equal the int64 value of sum_h w_h * sum_i q_hi K_bi exactly;
+  * a brute-force rank, a different algorithm from sorting: the selected
+    position of block b is c_b = #{b' admitted : s_b' > s_b or
+    (s_b' == s_b and b' < b)}, and b is selected iff c_b < k;
+  * fp64 evaluation with numpy's matmul and Higham's bound for recursive
+    summation (Accuracy and Stability of Numerical Algorithms, sec. 3.1:
+    |error| <= gamma_n * sum |terms|, gamma_n = n u / (1 - n u), u = 2**-24);
+  * special cases with closed forms and invariants of the problem.
+
+Each check takes the ctypes library so the mutation test can run the same
+checks against deliberately broken copies of the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from sparse_attention_block_ds_amd import workloads as wl
+
+
+# ---------------------------------------------------------------- helpers
+def admitted_mask(p: wl.Problem) -> np.ndarray:
+    """bool [L][R][N]: mask bit AND b < clamp(limit), straight from the definition."""
+    L, R, N = p.layers, p.rows, p.blocks
+    adm = np.ones((L, R, N), bool)
+    if p.mask is not None:
+        bits = np.unpackbits(p.mask.view(np.uint8), axis=-1, bitorder="little")[..., :N]
+        adm &= np.broadcast_to(bits.astype(bool), (L, R, N)) if bits.shape[1] == 1 else bits.astype(bool)
+    if p.limit is not None:
+        lim = np.clip(p.limit.astype(np.int64), 0, N)
+        adm &= np.arange(N)[None, None, :] < lim[:, :, None]
+    return adm
+
+
+def exact_int_scores(p: wl.Problem) -> np.ndarray:
+    """int64 [L][R][N] scores of integer-valued inputs, exactly."""
+    q = wl.bf16_bits_to_f32(p.q).astype(np.int64)
+    w = wl.bf16_bits_to_f32(p.w).astype(np.int64)
+    keys = wl.bf16_bits_to_f32(p.keys[:, :, :p.dim]).astype(np.int64)
+    assert np.all(q == wl.bf16_bits_to_f32(p.q)), "inputs must be integer-valued"
+    qt = np.einsum("lrh,lrhd->lrd", w, q)              # fold is exact on integers
+    return np.einsum("lrd,lnd->lrn", qt, keys)
+
+
+def f64_scores(p: wl.Problem):
+    """fp64 scores [L][R][N] and the magnitude sum_h |w_h| sum_i |q_hi K_bi|."""
+    q = wl.bf16_bits_to_f32(p.q).astype(np.float64)
+    w = wl.bf16_bits_to_f32(p.w).astype(np.float64)
+    keys = wl.bf16_bits_to_f32(p.keys[:, :, :p.dim]).astype(np.float64)
+    s = np.zeros((p.layers, p.rows, p.blocks))
+    mag = np.zeros_like(s)
+    for l in range(p.layers):
+        for r in range(p.rows):
+            per_head = q[l, r] @ keys[l].T                       # [H][N]
+            s[l, r] = w[l, r] @ per_head
+            mag[l, r] = np.abs(w[l, r]) @ (np.abs(q[l, r]) @ np.abs(keys[l]).T)
+    return s, mag
+
+
+def gamma(n: int) -> float:
+    u = 2.0 ** -24
+    return n * u / (1 - n * u)
+
+
+def brute_force_topk(scores: np.ndarray, admitted: np.ndarray, k: int):
+    """Selection by counting, O(n^2): returns (idx [k], score [k], count)."""
+    blocks = np.flatnonzero(admitted)
+    s = scores[blocks]
+    n = blocks.size
+    idx = np.full(k, -1, np.int64)
+    val = np.full(k, -np.inf)
+    if n:
+        beats = (s[None, :] > s[:, None]) | ((s[None, :] == s[:, None]) &
+                                             (blocks[None, :] < blocks[:, None]))
+        rank = beats.sum(axis=1)                   # distinct ranks 0..n-1
+        assert np.array_equal(np.sort(rank), np.arange(n))
+        take = rank < k
+        idx[rank[take]] = blocks[take]
+        val[rank[take]] = s[take]
+    return idx, val, min(k, n)
+
+
+def run(p: wl.Problem, lib, k=None):
+    return oracle.select(p.q, p.w, p.keys, p.k if k is None else k, p.mask, p.limit, lib=lib)
+
+
+# ---------------------------------------------------------------- checks
+def check_exact_integer(p: wl.Problem, lib):
+    """Integer-valued inputs: idx, score and count all exact."""
+    idx, score, count = run(p, lib)
+    exact = exact_int_scores(p)
+    assert np.abs(exact).max() < 2 ** 24
+    adm = admitted_mask(p)
+    for l in range(p.layers):
+        for r in range(p.rows):
+            e_idx, e_val, e_cnt = brute_force_topk(exact[l, r], adm[l, r], p.k)
+            assert count[l, r] == e_cnt, (l, r, count[l, r], e_cnt)
+            np.testing.assert_array_equal(idx[l, r], e_idx, err_msg=f"idx l={l} r={r}")
+            np.testing.assert_array_equal(score[l, r], e_val.astype(np.float32),
+                                          err_msg=f"score l={l} r={r}")
+
+
+def check_general_scores_within_bound(p: wl.Problem, lib):
+    """General inputs, k >= N: every admitted score within the fp32 rounding bound of fp64."""
+    idx, score, count = run(p, lib, k=max(1, p.blocks))
+    s64, mag = f64_scores(p)
+    adm = admitted_mask(p)
+    bound_factor = 2 * gamma(p.dim + p.heads)
+    for l in range(p.layers):
+        for r in range(p.rows):
+            n = int(adm[l, r].sum())
+            assert count[l, r] == n
+            blk = idx[l, r, :n]
+            assert np.array_equal(np.sort(blk), np.flatnonzero(adm[l, r]))
+            err = np.abs(score[l, r, :n].astype(np.float64) - s64[l, r, blk])
+            tol = bound_factor * mag[l, r, blk] + 1e-30
+            assert np.all(err <= tol), float(np.max(err / tol))
+            # the returned list is in the total order of the returned fp32 scores
+            sc = score[l, r, :n]
+            ok = (sc[:-1] > sc[1:]) | ((sc[:-1] == sc[1:]) & (blk[:-1] < blk[1:]))
+            assert np.all(ok)
+
+
+def check_invariants(p: wl.Problem, lib):
+    """Count, admission, uniqueness, order, selected >= unselected, prefix property."""
+    idx, score, count = run(p, lib)
+    full_idx, full_score, full_count = run(p, lib, k=max(1, p.blocks))
+    adm = admitted_mask(p)
+    for l in range(p.layers):
+        for r in range(p.rows):
+            n = int(adm[l, r].sum())
+            m = min(p.k, n)
+            assert count[l, r] == m and full_count[l, r] == n
+            sel = idx[l, r, :m]
+            assert np.all(adm[l, r][sel])
+            assert np.unique(sel).size == m
+            assert np.all(idx[l, r, m:] == -1) and np.all(np.isneginf(score[l, r, m:]))
+            # top-k is the prefix of the full order
+            np.testing.assert_array_equal(sel, full_idx[l, r, :m])
+            np.testing.assert_array_equal(score[l, r, :m], full_score[l, r, :m])
+            if m < n:
+                kth = score[l, r, m - 1]
+                rest = full_score[l, r, m:n]
+                assert np.all(rest <= kth)
+                tied_out = full_idx[l, r, m:n][rest == kth]
+                tied_in = sel[score[l, r, :m] == kth]
+                if tied_out.size:
+                    assert tied_in.max() < tied_out.min()
+
+
+def check_special_cases(lib):
+    """Closed forms: empty admission, k = 1, all-equal scores, H = 1 matvec, clamping."""
+    # empty: mask all zero, limit 0, N = 0
+    p = wl.make_custom(1, 2, 4, 64, 300, 16, seed=11, values="int3", mask_p=0.0)
+    idx, sc, cnt = run(p, lib)
+    assert np.all(cnt == 0) and np.all(idx == -1) and np.all(np.isneginf(sc))
+    p = wl.make_custom(1, 2, 4, 64, 300, 16, seed=12, values="int3", limits=0)
+    idx, sc, cnt = run(p, lib)
+    assert np.all(cnt == 0) and np.all(idx == -1)
+    p = wl.make_custom(1, 1, 4, 64, 0, 8, seed=13, values="int3")
+    idx, sc, cnt = run(p, lib)
+    assert np.all(cnt == 0) and np.all(idx == -1)
+    # negative limit clamps to 0, limit past N clamps to N
+    p = wl.make_custom(1, 2, 4, 64, 200, 300, seed=14, values="int3",
+                       limits=np.array([[-7, 10 ** 6]], np.int32))
+    idx, sc, cnt = run(p, lib)
+    assert cnt[0, 0] == 0 and cnt[0, 1] == 200
+    # k = 1 is the first maximum among admitted blocks
+    p = wl.make_custom(2, 3, 8, 64, 777, 1, seed=15, values="int3", mask_p=0.5, mask_shared=False)
+    idx, sc, cnt = run(p, lib)
+    ex = exact_int_scores(p)
+    adm = admitted_mask(p)
+    for l in range(2):
+        for r in range(3):
+            masked = np.where(adm[l, r], ex[l, r], np.iinfo(np.int64).min)
+            assert idx[l, r, 0] == int(np.argmax(masked))
+            assert sc[l, r, 0] == np.float32(masked.max())
+    # every score equal (K = 0): the first k admitted blocks, ascending, score +0
+    p = wl.make_custom(1, 2, 4, 64, 1000, 100, seed=16, values="zero_keys", mask_p=0.3)
+    idx, sc, cnt = run(p, lib)
+    adm = admitted_mask(p)
+    for r in range(2):
+        np.testing.assert_array_equal(idx[0, r], np.flatnonzero(adm[0, r])[:100])
+        assert np.all(sc[0, r] == 0) and not np.any(np.signbit(sc[0, r]))
+    # H = 1, w = 1: score is the plain matrix-vector product q . K_b
+    p = wl.make_custom(1, 1, 1, 128, 500, 500, seed=17, values="normal")
+    p.w[:] = wl.BF16_ONE
+    idx, sc, cnt = run(p, lib)
+    qf = wl.bf16_bits_to_f32(p.q[0, 0, 0]).astype(np.float64)
+    kf = wl.bf16_bits_to_f32(p.keys[0]).astype(np.float64)
+    mv = kf @ qf
+    bound = gamma(128) * (np.abs(kf) @ np.abs(qf))
+    assert np.all(np.abs(sc[0, 0].astype(np.float64) - mv[idx[0, 0]]) <= bound[idx[0, 0]])
+    # k >= n returns every admitted block: a permutation of the admitted set
+    assert cnt[0, 0] == 500 and np.array_equal(np.sort(idx[0, 0]), np.arange(500))
+
+
+def check_metamorphic(lib):
+    """Relations that hold whatever the exact scores are."""
+    # limit = L behaves like a mask holding bits [0, L)
+    p = wl.make_custom(1, 3, 8, 64, 900, 64, seed=21, values="normal", limits=np.array([[0, 333, 900]]))
+    a = run(p, lib)
+    bits = np.zeros((1, 3, 900), bool)
+    for r, lim in enumerate([0, 333, 900]):
+        bits[0, r, :lim] = True
+    p2 = wl.Problem("m", 64, p.q, p.w, p.keys, wl.pack_mask(bits), None)
+    b = run(p2, lib)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    # doubling w doubles every score exactly and keeps the selection
+    p = wl.make_custom(1, 2, 16, 64, 700, 50, seed=22, values="normal", mask_p=0.7)
+    a_idx, a_sc, _ = run(p, lib)
+    w2 = wl.f32_to_bf16_bits(wl.bf16_bits_to_f32(p.w) * 2)
+    p2 = wl.Problem("m", 50, p.q, w2, p.keys, p.mask, p.limit)
+    b_idx, b_sc, _ = run(p2, lib)
+    np.testing.assert_array_equal(a_idx, b_idx)
+    np.testing.assert_array_equal(a_sc * 2, b_sc)
+    # rows and layers are independent problems
+    p = wl.make_custom(2, 4, 8, 64, 600, 40, seed=23, values="int3", mask_p=0.6, mask_shared=False,
+                       limits=np.array([[600, 599, 598, 10], [5, 600, 300, 599]]))
+    whole = run(p, lib)
+    for l in range(2):
+        for r in range(4):
+            sub = wl.Problem("m", 40, p.q[l:l + 1, r:r + 1], p.w[l:l + 1, r:r + 1],
+                             p.keys[l:l + 1], p.mask[l:l + 1, r:r + 1], p.limit[l:l + 1, r:r + 1])
+            part = run(sub, lib)
+            for x, y in zip(whole, part):
+                np.testing.assert_array_equal(x[l, r], y[0, 0])
+    # a shared mask row is the same as that row repeated for every row
+    p = wl.make_custom(2, 3, 8, 64, 500, 30, seed=24, values="int3", mask_p=0.4)
+    rep = np.ascontiguousarray(np.repeat(p.mask, 3, axis=1))
+    p2 = wl.Problem("m", 30, p.q, p.w, p.keys, rep, p.limit)
+    for x, y in zip(run(p, lib), run(p2, lib)):
+        np.testing.assert_array_equal(x, y)
+    # key columns past d are never read (they hold NaN bit patterns)
+    p = wl.make_custom(1, 2, 8, 64, 400, 32, seed=25, values="int3", ldk=72)
+    p2 = wl.Problem("m", 32, p.q, p.w, np.ascontiguousarray(p.keys[:, :, :64]), None, None)
+    for x, y in zip(run(p, lib), run(p2, lib)):
+        np.testing.assert_array_equal(x, y)
+
+
+def all_pins(lib, include_slow=False):
+    """Every pin; raises AssertionError on the first failure."""
+    check_exact_integer(wl.make_custom(1, 1, 4, 64, 1500, 512, seed=0, values="int3"), lib)
+    check_exact_integer(wl.make_custom(2, 6, 16, 128, 1200, 256, seed=31, values="int3",
+                                       limits=np.array([[1200 - 5 + r for r in range(6)]] * 2)), lib)
+    check_exact_integer(wl.make_custom(3, 6, 16, 128, 2000, 300, seed=32, values="ternary",
+                                       mask_p=0.5, limits=np.array([[2000 - 5 + r for r in range(6)]] * 3)), lib)
+    check_exact_integer(wl.make_custom(1, 3, 4, 64, 800, 100, seed=33, values="int3",
+                                       mask_p=0.3, mask_shared=False), lib)
+    check_general_scores_within_bound(wl.make_custom(1, 2, 64, 128, 700, 512, seed=34,
+                                                     values="normal", mask_p=0.6), lib)
+    check_invariants(wl.make_custom(1, 1, 64, 128, 2048, 512, seed=35, values="normal"), lib)
+    check_invariants(wl.make_custom(2, 3, 8, 64, 1500, 200, seed=36, values="ternary",
+                                    mask_p=0.5), lib)
+    check_special_cases(lib)
+    check_metamorphic(lib)
+    if include_slow:
+        check_exact_integer(wl.make("tiny"), lib)

@@ -1,0 +1,52 @@
+"""Plant one plausible mistake at a time in a copy of the CPU oracle and check
+that the pins catch every one.  The copies are built in a temporary folder;
+the real oracle source is never modified."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import pins
+
+# (name, text in ds_sel_oracle.c, replacement)
+MUTANTS = [
+    ("drop_last_head", "for (int h = 0; h < heads; ++h) {", "for (int h = 0; h < heads - 1; ++h) {"),
+    ("drop_last_dim", "for (int i = 0; i < dim; ++i) {", "for (int i = 0; i < dim - 1; ++i) {"),
+    ("ignore_head_weight", "float t = bf16_bits_to_float(w_row[h]) * dot;", "float t = dot;"),
+    ("head_index_reversed", "const uint16_t* qh = q_row + (int64_t)h * dim;",
+     "const uint16_t* qh = q_row + (int64_t)(heads - 1 - h) * dim;"),
+    ("sign_flip", "s = s + t;", "s = s - t;"),
+    ("tie_to_higher_index", "if (a->block < b->block) return -1;", "if (a->block < b->block) return 1;"),
+    ("ascending_order", "if (a->score > b->score) return -1;", "if (a->score > b->score) return 1;"),
+    ("limit_drops_last", "for (int64_t b = 0; b < lim; ++b) {", "for (int64_t b = 0; b + 1 < lim; ++b) {"),
+    ("mask_bit_order_reversed", "(uint32_t)(b & 31)", "(uint32_t)(31 - (b & 31))"),
+    ("mask_ignored", "if (mrow && !mask_bit(mrow, b)) continue;", ""),
+    ("no_limit_clamp_low", "if (v < 0) v = 0;", "if (v < 0) v = -v;"),
+    ("padding_score_zero", "os[j] = -INFINITY;", "os[j] = 0.0f;"),
+    ("count_is_admitted", "if (out_count) out_count[lr] = (int32_t)m;",
+     "if (out_count) out_count[lr] = (int32_t)n;"),
+    ("wrong_row_of_w", "const uint16_t* w_row = w + lr * heads;", "const uint16_t* w_row = w + (int64_t)l * rows * heads;"),
+    ("shared_mask_ignores_row", "mask + l * mask_layer_stride + r * mask_row_stride",
+     "mask + l * mask_layer_stride"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / "libmutant.so")
+    oracle.build(output=lib_path, source=str(mutant_src))
+    lib = oracle.load(lib_path)
+    with pytest.raises((AssertionError, oracle.OracleError)):
+        pins.all_pins(lib)
+
+
+def test_unmutated_copy_passes(tmp_path):
+    lib_path = str(tmp_path / "libcopy.so")
+    oracle.build(output=lib_path)
+    pins.all_pins(oracle.load(lib_path))
