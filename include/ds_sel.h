@@ -1,0 +1,160 @@
+/*
+ * ds_sel.h -- compressed-attention block selection on AMD MI355X (gfx950).
+ *
+ * The operation (page "DeepSeek V4.1F Q4 on M3 Ultra with native DSpark MTP
+ * (40tps / 800tps)", paragraph "Decode at depth"; restated on page "DeepSeek
+ * V4.1 Flash on M3 Ultra nearly doubles decode to 31 t/s with first public
+ * DSpark Metal port", paragraph "Key techniques"): in every layer the
+ * compressed attention keeps k = 512 compressed blocks chosen from the whole
+ * context.  Only blocks that a row's admission mask lets through are scored,
+ * the admitted index is compacted once per row, and the best k are taken with
+ * a radix select whose number of passes is bounded.  With the speculative
+ * drafter on, one decode step verifies several query rows that share one
+ * stream of data (same page, paragraph "DSpark"); here the rows of one layer
+ * share one pass over the block keys.
+ *
+ * The pages give no formula.  This library defines, for layer l, row r and
+ * block b (readings of this library):
+ *
+ *   admitted(l,r,b) = (mask == NULL or bit b of the (l,r) mask row is 1)
+ *                     and b < clamp(limit[l][r], 0, N)     (limit NULL -> N)
+ *   score(l,r,b)    = sum_h w[l][r][h] * (q[l][r][h][:] . K[l][b][:])
+ *                     with bf16 inputs and fp32 accumulation
+ *   order           = higher score first; equal scores -> lower block index
+ *   result(l,r)     = the first m = min(k, #admitted) blocks in that order,
+ *                     then k - m padding entries (index -1, score -inf);
+ *                     count = m.
+ *
+ * The GPU evaluates the score as (sum_h w_h q_h) . K_b in fp32 (the sum is
+ * linear, so folding the heads first is the same sum).  On inputs whose bf16
+ * values are small integers every partial sum is exact and the result is
+ * bit-identical to any other fp32 evaluation order; on general inputs scores
+ * differ from a per-head evaluation only by fp32 rounding.  The order is taken
+ * on the GPU's own fp32 scores, so the output is always consistent with the
+ * scores it returns.
+ *
+ * Conventions for every entry point:
+ *   - Integer status codes, 0 = success; no exceptions or longjmps cross the
+ *     ABI.  ds_sel_status_string() names a code.
+ *   - Argument, alignment and capacity checks run on the host before anything
+ *     is enqueued; on DS_SEL_E_INVALID, DS_SEL_E_UNSUPPORTED or
+ *     DS_SEL_E_CAPACITY nothing runs and the outputs are untouched.
+ *   - All data pointers in ds_sel_args are DEVICE pointers on the handle's
+ *     device, owned by the caller.  The library keeps none of them after the
+ *     enqueued work completes.
+ */
+#ifndef DS_SEL_H
+#define DS_SEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DS_SEL_OK = 0,
+  DS_SEL_E_INVALID = 1,     /* bad argument: null, negative, misaligned, inconsistent */
+  DS_SEL_E_CAPACITY = 2,    /* exceeds the capacity declared at ds_sel_create */
+  DS_SEL_E_NODEVICE = 3,    /* no HIP device, or the ordinal does not exist */
+  DS_SEL_E_HIP = 4,         /* a HIP runtime call or launch failed */
+  DS_SEL_E_NOMEM = 5,       /* device or host allocation failed */
+  DS_SEL_E_UNSUPPORTED = 6  /* valid but not built: dim outside {32, 64, 128, 256} */
+};
+
+/* Hard limits of this build (a capacity above them is DS_SEL_E_INVALID). */
+#define DS_SEL_MAX_ROWS 8
+#define DS_SEL_MAX_K 2048
+#define DS_SEL_MAX_HEADS 1024
+#define DS_SEL_MAX_DIM 256
+#define DS_SEL_MAX_BLOCKS (1LL << 26)
+
+typedef struct ds_sel ds_sel; /* opaque handle; owns device scratch */
+
+/* Create-time capacity.  Every call on the handle must fit inside it. */
+typedef struct {
+  uint32_t struct_size; /* sizeof(ds_sel_limits) */
+  int32_t device;       /* HIP device ordinal the handle lives on */
+  int32_t max_layers;   /* >= 1 */
+  int32_t max_rows;     /* 1 .. DS_SEL_MAX_ROWS */
+  int32_t max_heads;    /* 1 .. DS_SEL_MAX_HEADS */
+  int32_t max_dim;      /* 1 .. DS_SEL_MAX_DIM */
+  int32_t max_k;        /* 1 .. DS_SEL_MAX_K */
+  int32_t reserved;     /* must be 0 */
+  int64_t max_blocks;   /* 0 .. DS_SEL_MAX_BLOCKS */
+} ds_sel_limits;
+
+/* One call: `layers` independent selection problems, each with `rows` query
+ * rows that share the layer's block keys.  Element strides, not bytes. */
+typedef struct {
+  uint32_t struct_size; /* sizeof(ds_sel_args) */
+  int32_t layers;       /* L >= 1 */
+  int32_t rows;         /* R, 1 .. DS_SEL_MAX_ROWS */
+  int32_t heads;        /* H >= 1 */
+  int32_t dim;          /* d in {32, 64, 128, 256} */
+  int32_t k;            /* 1 .. max_k; k > #admitted is allowed (padding) */
+  int64_t blocks;       /* N >= 0 */
+  const void* q;        /* bf16 [L][R][H][d], contiguous */
+  const void* w;        /* bf16 [L][R][H], contiguous */
+  const void* keys;     /* bf16; block b of layer l at keys + l*key_layer_stride + b*ldk;
+                           16-byte aligned; may be NULL only when N == 0 */
+  int64_t ldk;          /* >= d, multiple of 8 */
+  int64_t key_layer_stride; /* multiple of 8; >= N*ldk when L > 1 */
+  const uint32_t* mask; /* NULL (admit all), or words; the (l,r) row starts at
+                           mask + l*mask_layer_stride + r*mask_row_stride; bit b%32 of
+                           word b/32 (LSB first); bits at b >= N are ignored */
+  int64_t mask_row_stride;   /* 0 = one row shared by all rows of a layer, else >= ceil(N/32) */
+  int64_t mask_layer_stride; /* >= (R-1)*mask_row_stride + ceil(N/32) when L > 1 */
+  const int32_t* limit; /* NULL (limit N), or int32 [L][R]; admitted iff b < limit, and the
+                           value is clamped to [0, N] on the device */
+  int32_t* out_idx;     /* int32 [L][R][k] */
+  float* out_score;     /* float [L][R][k] */
+  int32_t* out_count;   /* int32 [L][R], or NULL */
+} ds_sel_args;
+
+/* Create a handle on lim->device with scratch for the declared capacity.
+ * Returns DS_SEL_E_NODEVICE when there is no HIP device (also on a host with
+ * no GPU at all), DS_SEL_E_INVALID for a bad capacity, DS_SEL_E_NOMEM when
+ * the scratch cannot be allocated.  On success *out owns the handle. */
+int ds_sel_create(const ds_sel_limits* lim, ds_sel** out);
+
+/* Enqueue the whole chain for one call on `hip_stream` (a hipStream_t on the
+ * handle's device; NULL = the null stream) and return without waiting.  The
+ * outputs are valid once the stream reaches this point; inputs must not change
+ * before then.  Calls on one handle must be ordered on one stream (they reuse
+ * its scratch); the handle is not thread-safe.  DS_SEL_E_HIP means a launch
+ * failed: outputs are undefined and the handle stays usable. */
+int ds_sel_score_select(ds_sel* h, const ds_sel_args* a, void* hip_stream);
+
+/* The same work as ds_sel_score_select, plus a per-dispatch ledger: the
+ * four caller-created hipEvent_t in `events` are recorded on `hip_stream`
+ * before the first kernel and after each of the three (prep, score, select),
+ * so hipEventElapsedTime between consecutive events gives each kernel's
+ * device time.  Same status codes; on an argument error no event is recorded.
+ * (The pages keep a per-dispatch bandwidth ledger for the same purpose: page
+ * "DeepSeek V4.1F Q4 on M3 Ultra with native DSpark MTP (40tps / 800tps)",
+ * the paragraph listing what else the repository holds.) */
+int ds_sel_score_select_profiled(ds_sel* h, const ds_sel_args* a, void* hip_stream,
+                                 void* const events[4]);
+
+/* Free the handle and its scratch (waits for the device to finish using it).
+ * NULL is a no-op. */
+void ds_sel_destroy(ds_sel* h);
+
+/* The host-side checks ds_sel_score_select applies, without a device:
+ * DS_SEL_OK if `a` is acceptable for a handle created with `lim`.  Pointer
+ * values are only checked for NULL and alignment, never dereferenced. */
+int ds_sel_check_args(const ds_sel_limits* lim, const ds_sel_args* a);
+
+/* Bytes of device scratch a handle with capacity `lim` allocates (0 on a bad
+ * capacity). */
+int64_t ds_sel_scratch_bytes(const ds_sel_limits* lim);
+
+/* A static string naming a status code. */
+const char* ds_sel_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DS_SEL_H */

@@ -1,0 +1,83 @@
+// Device helpers shared by the libdssel kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dssel {
+
+constexpr int kWave = 64;
+
+// Order-preserving map from an fp32 score to a uint32 radix key: a larger
+// score gives a larger key, and the map is a bijection on bit patterns once
+// -0 has been folded onto +0 (so the score is recovered from its key).
+__device__ __forceinline__ uint32_t score_to_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_score(uint32_t key) {
+  uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
+}
+
+// bf16 halves of a 32-bit word, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum across a workgroup of NT threads (NT a multiple of 64,
+// at most 64 waves).  `scratch` must hold NT/64 + 1 ints of LDS.  Every thread
+// of the workgroup must call it; it contains two barriers and leaves the
+// scratch reusable after the final barrier.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* scratch) {
+  constexpr int kWaves = NT / kWave;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int incl = wave_inclusive_scan(v);
+  if (lane == kWave - 1) scratch[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int x = lane < kWaves ? scratch[lane] : 0;
+    int xi = wave_inclusive_scan(x);
+    if (lane < kWaves) scratch[lane] = xi - x;
+    if (lane == kWaves - 1) scratch[kWaves] = xi;
+  }
+  __syncthreads();
+  const int result = scratch[wave] + incl - v;
+  *total = scratch[kWaves];
+  __syncthreads();
+  return result;
+}
+
+// Append the calling lane's item to an LDS list with one atomic per wave.
+// Returns the slot index for lanes with `want`, -1 otherwise.  Must be
+// called by every active lane of the wave (uniform control flow).
+__device__ __forceinline__ int wave_append(bool want, int* counter) {
+  const uint64_t ballot = __ballot(want);
+  if (ballot == 0) return -1;
+  const int leader = __ffsll((long long)ballot) - 1;
+  const int lane = lane_id();
+  const int n = __popcll(ballot);
+  int base = 0;
+  if (lane == leader) base = atomicAdd(counter, n);
+  base = __shfl(base, leader, kWave);
+  const uint64_t below = ballot & ((lane == 0) ? 0ull : (~0ull >> (kWave - lane)));
+  return want ? base + __popcll(below) : -1;
+}
+
+}  // namespace dssel

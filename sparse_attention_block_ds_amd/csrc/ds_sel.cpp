@@ -1,0 +1,245 @@
+// libdssel host side: the C ABI of include/ds_sel.h.  Validates every call on
+// the host, owns the device scratch, and enqueues the three kernels (prep ->
+// score -> select) on the caller's stream without synchronising.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "ds_sel.h"
+#include "dssel_internal.h"
+
+struct ds_sel {
+  ds_sel_limits lim;
+  void* scratch = nullptr;
+  int64_t scratch_bytes = 0;
+  // offsets into scratch
+  int64_t off_qt = 0, off_list = 0, off_counts = 0, off_keys = 0, off_hist = 0;
+};
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  int64_t qt, list, counts, keys, hist, total;
+};
+
+// Scratch for a capacity: q~ fp32 [L][R][d], index int32 [L][N], counts
+// int32 [L][9], radix keys uint32 [L][R][N], histograms uint32 [L][R][2048].
+Layout layout_for(const ds_sel_limits& lim) {
+  Layout s{};
+  const int64_t L = lim.max_layers, R = lim.max_rows, D = lim.max_dim, N = lim.max_blocks;
+  int64_t off = 0;
+  s.qt = off;     off += align_up(L * R * D * 4);
+  s.list = off;   off += align_up(L * N * 4);
+  s.counts = off; off += align_up(L * dssel::kCountStride * 4);
+  s.keys = off;   off += align_up(L * R * N * 4);
+  s.hist = off;   off += align_up(L * R * dssel::kHistBins * 4);
+  s.total = off;
+  return s;
+}
+
+int check_limits(const ds_sel_limits* lim) {
+  if (!lim || lim->struct_size != sizeof(ds_sel_limits)) return DS_SEL_E_INVALID;
+  if (lim->max_layers < 1 || lim->max_layers > 65535) return DS_SEL_E_INVALID;
+  if (lim->max_rows < 1 || lim->max_rows > DS_SEL_MAX_ROWS) return DS_SEL_E_INVALID;
+  if (lim->max_heads < 1 || lim->max_heads > DS_SEL_MAX_HEADS) return DS_SEL_E_INVALID;
+  if (lim->max_dim < 1 || lim->max_dim > DS_SEL_MAX_DIM) return DS_SEL_E_INVALID;
+  if (lim->max_k < 1 || lim->max_k > DS_SEL_MAX_K) return DS_SEL_E_INVALID;
+  if (lim->max_blocks < 0 || lim->max_blocks > DS_SEL_MAX_BLOCKS) return DS_SEL_E_INVALID;
+  if (lim->reserved != 0 || lim->device < 0) return DS_SEL_E_INVALID;
+  return DS_SEL_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_args(const ds_sel_limits& lim, const ds_sel_args* a) {
+  if (!a || a->struct_size != sizeof(ds_sel_args)) return DS_SEL_E_INVALID;
+  if (a->layers < 1 || a->rows < 1 || a->heads < 1 || a->dim < 1 || a->k < 1 || a->blocks < 0)
+    return DS_SEL_E_INVALID;
+  if (a->rows > DS_SEL_MAX_ROWS || a->k > DS_SEL_MAX_K || a->heads > DS_SEL_MAX_HEADS ||
+      a->blocks > DS_SEL_MAX_BLOCKS)
+    return DS_SEL_E_INVALID;
+  if (a->dim != 32 && a->dim != 64 && a->dim != 128 && a->dim != 256) {
+    if (a->dim % 8 != 0 || a->dim > DS_SEL_MAX_DIM) return DS_SEL_E_INVALID;
+    return DS_SEL_E_UNSUPPORTED;
+  }
+  if (a->layers > lim.max_layers || a->rows > lim.max_rows || a->heads > lim.max_heads ||
+      a->dim > lim.max_dim || a->k > lim.max_k || a->blocks > lim.max_blocks)
+    return DS_SEL_E_CAPACITY;
+  if (!a->q || !a->w || !a->out_idx || !a->out_score) return DS_SEL_E_INVALID;
+  if (!aligned(a->q, 2) || !aligned(a->w, 2) || !aligned(a->out_idx, 4) ||
+      !aligned(a->out_score, 4) || !aligned(a->out_count, 4) || !aligned(a->limit, 4) ||
+      !aligned(a->mask, 4))
+    return DS_SEL_E_INVALID;
+  const int64_t N = a->blocks;
+  if (N > 0) {
+    if (!a->keys || !aligned(a->keys, 16)) return DS_SEL_E_INVALID;
+    if (a->ldk < a->dim || a->ldk % 8 != 0) return DS_SEL_E_INVALID;
+    if (a->key_layer_stride < 0 || a->key_layer_stride % 8 != 0) return DS_SEL_E_INVALID;
+    if (a->layers > 1 && a->key_layer_stride < N * a->ldk) return DS_SEL_E_INVALID;
+  }
+  if (a->mask) {
+    const int64_t words = (N + 31) / 32;
+    if (a->mask_row_stride != 0 && a->mask_row_stride < words) return DS_SEL_E_INVALID;
+    if (a->mask_row_stride < 0 || a->mask_layer_stride < 0) return DS_SEL_E_INVALID;
+    if (a->layers > 1 && a->mask_layer_stride < (a->rows - 1) * a->mask_row_stride + words)
+      return DS_SEL_E_INVALID;
+  }
+  return DS_SEL_OK;
+}
+
+// Runs f with `device` current and restores the caller's device.
+template <class F>
+int with_device(int device, F f) {
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return DS_SEL_E_HIP;
+  if (prev != device && hipSetDevice(device) != hipSuccess) return DS_SEL_E_HIP;
+  const int rc = f();
+  if (prev != device) (void)hipSetDevice(prev);
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ds_sel_status_string(int status) {
+  switch (status) {
+    case DS_SEL_OK: return "ok";
+    case DS_SEL_E_INVALID: return "invalid argument";
+    case DS_SEL_E_CAPACITY: return "exceeds the handle's capacity";
+    case DS_SEL_E_NODEVICE: return "no such HIP device";
+    case DS_SEL_E_HIP: return "HIP runtime error";
+    case DS_SEL_E_NOMEM: return "out of memory";
+    case DS_SEL_E_UNSUPPORTED: return "unsupported dimension";
+    default: return "unknown status";
+  }
+}
+
+int64_t ds_sel_scratch_bytes(const ds_sel_limits* lim) {
+  if (check_limits(lim) != DS_SEL_OK) return 0;
+  return layout_for(*lim).total;
+}
+
+int ds_sel_check_args(const ds_sel_limits* lim, const ds_sel_args* a) {
+  const int rc = check_limits(lim);
+  if (rc != DS_SEL_OK) return rc;
+  return check_args(*lim, a);
+}
+
+int ds_sel_create(const ds_sel_limits* lim, ds_sel** out) {
+  if (!out) return DS_SEL_E_INVALID;
+  *out = nullptr;
+  int rc = check_limits(lim);
+  if (rc != DS_SEL_OK) return rc;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return DS_SEL_E_NODEVICE;
+  }
+  if (lim->device >= ndev) return DS_SEL_E_NODEVICE;
+  ds_sel* h = new (std::nothrow) ds_sel;
+  if (!h) return DS_SEL_E_NOMEM;
+  h->lim = *lim;
+  const Layout s = layout_for(*lim);
+  rc = with_device(lim->device, [&]() {
+    if (hipMalloc(&h->scratch, (size_t)s.total) != hipSuccess) {
+      (void)hipGetLastError();
+      h->scratch = nullptr;
+      return (int)DS_SEL_E_NOMEM;
+    }
+    return (int)DS_SEL_OK;
+  });
+  if (rc != DS_SEL_OK) {
+    delete h;
+    return rc;
+  }
+  h->scratch_bytes = s.total;
+  h->off_qt = s.qt;
+  h->off_list = s.list;
+  h->off_counts = s.counts;
+  h->off_keys = s.keys;
+  h->off_hist = s.hist;
+  *out = h;
+  return DS_SEL_OK;
+}
+
+void ds_sel_destroy(ds_sel* h) {
+  if (!h) return;
+  if (h->scratch) {
+    with_device(h->lim.device, [&]() {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(h->scratch);
+      return (int)DS_SEL_OK;
+    });
+  }
+  delete h;
+}
+
+namespace {
+int enqueue(ds_sel* h, const ds_sel_args* a, void* hip_stream, void* const* events);
+}
+
+int ds_sel_score_select(ds_sel* h, const ds_sel_args* a, void* hip_stream) {
+  return enqueue(h, a, hip_stream, nullptr);
+}
+
+int ds_sel_score_select_profiled(ds_sel* h, const ds_sel_args* a, void* hip_stream,
+                                 void* const events[4]) {
+  if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return DS_SEL_E_INVALID;
+  return enqueue(h, a, hip_stream, events);
+}
+
+}  // extern "C"
+
+namespace {
+int enqueue(ds_sel* h, const ds_sel_args* a, void* hip_stream, void* const* events) {
+  if (!h) return DS_SEL_E_INVALID;
+  int rc = check_args(h->lim, a);
+  if (rc != DS_SEL_OK) return rc;
+
+  dssel::Call c{};
+  c.layers = a->layers;
+  c.rows = a->rows;
+  c.heads = a->heads;
+  c.dim = a->dim;
+  c.k = a->k;
+  c.blocks = a->blocks;
+  c.q = static_cast<const uint16_t*>(a->q);
+  c.w = static_cast<const uint16_t*>(a->w);
+  c.keys = static_cast<const uint16_t*>(a->keys);
+  c.ldk = a->ldk;
+  c.key_layer_stride = a->key_layer_stride;
+  c.mask = a->mask;
+  c.mask_row_stride = a->mask_row_stride;
+  c.mask_layer_stride = a->mask_layer_stride;
+  c.limit = a->limit;
+  c.mode = !a->mask ? dssel::kNoMask
+                    : ((a->mask_row_stride == 0 || a->rows == 1) ? dssel::kSharedMask
+                                                                 : dssel::kRowMask);
+  c.out_idx = a->out_idx;
+  c.out_score = a->out_score;
+  c.out_count = a->out_count;
+  char* base = static_cast<char*>(h->scratch);
+  c.qt = reinterpret_cast<float*>(base + h->off_qt);
+  c.list = reinterpret_cast<int32_t*>(base + h->off_list);
+  c.counts = reinterpret_cast<int32_t*>(base + h->off_counts);
+  c.skeys = reinterpret_cast<uint32_t*>(base + h->off_keys);
+  c.hist = reinterpret_cast<uint32_t*>(base + h->off_hist);
+
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  auto mark = [&](int i) {
+    return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) == hipSuccess;
+  };
+  return with_device(h->lim.device, [&]() {
+    if (!mark(0)) return (int)DS_SEL_E_HIP;
+    if (dssel::launch_prep(c, stream) != hipSuccess || !mark(1)) return (int)DS_SEL_E_HIP;
+    if (dssel::launch_score(c, stream) != hipSuccess || !mark(2)) return (int)DS_SEL_E_HIP;
+    if (dssel::launch_select(c, stream) != hipSuccess || !mark(3)) return (int)DS_SEL_E_HIP;
+    return (int)DS_SEL_OK;
+  });
+}
+}  // namespace

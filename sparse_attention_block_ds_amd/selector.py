@@ -1,0 +1,200 @@
+"""ctypes binding of libdssel (include/ds_sel.h) for torch tensors.
+
+Marshalling only: every step of the selection runs in the library's HIP
+kernels.  torch provides device memory and the stream.  If the library is not
+built this module raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libdssel.so")
+
+DS_SEL_OK = 0
+DS_SEL_E_INVALID = 1
+DS_SEL_E_CAPACITY = 2
+DS_SEL_E_NODEVICE = 3
+DS_SEL_E_HIP = 4
+DS_SEL_E_NOMEM = 5
+DS_SEL_E_UNSUPPORTED = 6
+
+EXPORTED = ("ds_sel_create", "ds_sel_score_select", "ds_sel_score_select_profiled",
+            "ds_sel_destroy", "ds_sel_check_args", "ds_sel_scratch_bytes", "ds_sel_status_string")
+
+
+class Limits(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("device", ctypes.c_int32),
+                ("max_layers", ctypes.c_int32), ("max_rows", ctypes.c_int32),
+                ("max_heads", ctypes.c_int32), ("max_dim", ctypes.c_int32),
+                ("max_k", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int64)]
+
+
+class Args(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("layers", ctypes.c_int32),
+                ("rows", ctypes.c_int32), ("heads", ctypes.c_int32), ("dim", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("blocks", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("w", ctypes.c_void_p), ("keys", ctypes.c_void_p),
+                ("ldk", ctypes.c_int64), ("key_layer_stride", ctypes.c_int64),
+                ("mask", ctypes.c_void_p), ("mask_row_stride", ctypes.c_int64),
+                ("mask_layer_stride", ctypes.c_int64), ("limit", ctypes.c_void_p),
+                ("out_idx", ctypes.c_void_p), ("out_score", ctypes.c_void_p),
+                ("out_count", ctypes.c_void_p)]
+
+
+class DsSelError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIBRARY):
+    """Load libdssel.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m sparse_attention_block_ds_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.ds_sel_create.argtypes = [P(Limits), P(ctypes.c_void_p)]
+    lib.ds_sel_create.restype = ctypes.c_int
+    lib.ds_sel_score_select.argtypes = [ctypes.c_void_p, P(Args), ctypes.c_void_p]
+    lib.ds_sel_score_select.restype = ctypes.c_int
+    lib.ds_sel_score_select_profiled.argtypes = [ctypes.c_void_p, P(Args), ctypes.c_void_p,
+                                                 P(ctypes.c_void_p)]
+    lib.ds_sel_score_select_profiled.restype = ctypes.c_int
+    lib.ds_sel_destroy.argtypes = [ctypes.c_void_p]
+    lib.ds_sel_destroy.restype = None
+    lib.ds_sel_check_args.argtypes = [P(Limits), P(Args)]
+    lib.ds_sel_check_args.restype = ctypes.c_int
+    lib.ds_sel_scratch_bytes.argtypes = [P(Limits)]
+    lib.ds_sel_scratch_bytes.restype = ctypes.c_int64
+    lib.ds_sel_status_string.argtypes = [ctypes.c_int]
+    lib.ds_sel_status_string.restype = ctypes.c_char_p
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().ds_sel_status_string(status).decode()
+    except RuntimeError:
+        return "status"
+
+
+def make_limits(max_layers, max_rows, max_heads, max_dim, max_blocks, max_k=512, device=0):
+    return Limits(ctypes.sizeof(Limits), device, max_layers, max_rows, max_heads, max_dim, max_k,
+                  0, max_blocks)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_args(q, w, keys, k, mask=None, limit=None, out_idx=None, out_score=None, out_count=None):
+    """Fill an Args struct from tensors (no checks beyond shapes; the library validates)."""
+    L, R, H, d = q.shape
+    N = keys.shape[1]
+    a = Args()
+    a.struct_size = ctypes.sizeof(Args)
+    a.layers, a.rows, a.heads, a.dim, a.k, a.blocks = L, R, H, d, k, N
+    a.q, a.w = _ptr(q), _ptr(w)
+    a.keys = _ptr(keys) if N > 0 else None
+    a.ldk = keys.stride(1)
+    a.key_layer_stride = keys.stride(0)
+    if mask is not None:
+        a.mask = _ptr(mask)
+        a.mask_row_stride = 0 if mask.shape[1] == 1 else mask.stride(1)
+        a.mask_layer_stride = mask.stride(0)
+    a.limit = _ptr(limit)
+    a.out_idx, a.out_score, a.out_count = _ptr(out_idx), _ptr(out_score), _ptr(out_count)
+    return a
+
+
+class Selector:
+    """One libdssel handle: scratch sized for the given capacity on one device."""
+
+    def __init__(self, max_layers, max_rows, max_heads, max_dim, max_blocks, max_k=512,
+                 device: Optional[int] = None):
+        import torch
+        self._torch = torch
+        self.lib = load_library()
+        self.device = torch.cuda.current_device() if device is None else device
+        self.limits = make_limits(max_layers, max_rows, max_heads, max_dim, max_blocks, max_k,
+                                  self.device)
+        h = ctypes.c_void_p()
+        rc = self.lib.ds_sel_create(ctypes.byref(self.limits), ctypes.byref(h))
+        if rc != DS_SEL_OK:
+            raise DsSelError(rc, "ds_sel_create")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.ds_sel_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def score_select(self, q, w, keys, k, mask=None, limit=None, out=None, stream=None,
+                     events=None):
+        """Enqueue one call; returns (idx int32 [L,R,k], score f32 [L,R,k], count int32 [L,R]).
+
+        q bf16 [L,R,H,d]; w bf16 [L,R,H]; keys bf16 [L,N,ldk] (unit stride in the
+        last dim); mask int32 (bit patterns) [L, R or 1, words] or None; limit
+        int32 [L,R] or None.  The work is asynchronous on `stream` (default:
+        torch's current stream).  `events`: four torch.cuda.Event(enable_timing=True)
+        recorded before prep and after prep, score and select.
+        """
+        torch = self._torch
+        L, R = q.shape[0], q.shape[1]
+        if out is None:
+            out = (torch.empty((L, R, k), dtype=torch.int32, device=q.device),
+                   torch.empty((L, R, k), dtype=torch.float32, device=q.device),
+                   torch.empty((L, R), dtype=torch.int32, device=q.device))
+        a = make_args(q, w, keys, k, mask, limit, *out)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        if events is None:
+            rc = self.lib.ds_sel_score_select(self.handle, ctypes.byref(a), ctypes.c_void_p(handle))
+        else:
+            ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+            rc = self.lib.ds_sel_score_select_profiled(self.handle, ctypes.byref(a),
+                                                       ctypes.c_void_p(handle), ev)
+        if rc != DS_SEL_OK:
+            raise DsSelError(rc, "ds_sel_score_select")
+        return out
+
+
+def upload(problem, device="cuda"):
+    """Copy a workloads.Problem's host arrays to device tensors (bf16 bit patterns kept)."""
+    import torch
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    q = bf16(problem.q)
+    w = bf16(problem.w)
+    keys = bf16(problem.keys)
+    mask = None
+    if problem.mask is not None:
+        mask = torch.from_numpy(np.ascontiguousarray(problem.mask).view(np.int32)).to(device)
+    limit = None
+    if problem.limit is not None:
+        limit = torch.from_numpy(np.ascontiguousarray(problem.limit, dtype=np.int32)).to(device)
+    return q, w, keys, mask, limit

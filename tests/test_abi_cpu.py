@@ -1,0 +1,197 @@
+"""The C ABI without a GPU: exports, struct layout, host-side validation,
+and the no-device path.  No compute call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_attention_block_ds_amd import selector as sel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ds_sel.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sel.LIBRARY):
+        from sparse_attention_block_ds_amd import build
+        build.build(verbose=False)
+    return sel.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(ds_sel_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("ds_sel_create", "ds_sel_score_select", "ds_sel_destroy"):
+        assert required in names
+    assert set(names) == set(sel.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", sel.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ds_sel_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "ds_sel.h"
+#define F(T, m) printf(#T "." #m " %zu\n", offsetof(T, m))
+int main(void) {
+  printf("ds_sel_limits %zu\nds_sel_args %zu\n", sizeof(ds_sel_limits), sizeof(ds_sel_args));
+  F(ds_sel_limits, max_blocks); F(ds_sel_args, blocks); F(ds_sel_args, q); F(ds_sel_args, ldk);
+  F(ds_sel_args, mask); F(ds_sel_args, mask_layer_stride); F(ds_sel_args, limit);
+  F(ds_sel_args, out_count);
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    lines = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                   check=True).stdout.splitlines())
+    assert int(lines["ds_sel_limits"]) == ctypes.sizeof(sel.Limits)
+    assert int(lines["ds_sel_args"]) == ctypes.sizeof(sel.Args)
+    for key, value in lines.items():
+        if "." in key:
+            struct, field = key.split(".")
+            cls = sel.Limits if struct == "ds_sel_limits" else sel.Args
+            assert getattr(cls, field).offset == int(value), key
+
+
+class FakeTensor:
+    """Stands in for a device tensor: a pointer value that is never dereferenced."""
+
+    def __init__(self, shape, strides=None, ptr=0x10000):
+        self.shape = shape
+        self._strides = strides or tuple(int(x) for x in _contig(shape))
+        self._ptr = ptr
+
+    def data_ptr(self):
+        return self._ptr
+
+    def stride(self, i):
+        return self._strides[i]
+
+
+def _contig(shape):
+    out, acc = [], 1
+    for s in reversed(shape):
+        out.append(acc)
+        acc *= s
+    return tuple(reversed(out))
+
+
+def _args(L=2, R=6, H=64, d=128, N=75000, k=512, mask_rows=1, with_limit=True, ldk=None,
+          keys_ptr=0x20000):
+    ldk = ldk or d
+    q = FakeTensor((L, R, H, d), ptr=0x1000)
+    w = FakeTensor((L, R, H), ptr=0x3000)
+    keys = FakeTensor((L, N, ldk), (N * ldk, ldk, 1), ptr=keys_ptr)
+    words = (N + 31) // 32
+    mask = FakeTensor((L, mask_rows, words), ptr=0x40000) if mask_rows else None
+    limit = FakeTensor((L, R), ptr=0x50000) if with_limit else None
+    outs = (FakeTensor((L, R, k), ptr=0x60000), FakeTensor((L, R, k), ptr=0x70000),
+            FakeTensor((L, R), ptr=0x80000))
+    return sel.make_args(q, w, keys, k, mask, limit, *outs)
+
+
+LIM = dict(max_layers=43, max_rows=6, max_heads=64, max_dim=128, max_blocks=75000, max_k=512)
+
+
+def check(lib, args, **lim):
+    limits = sel.make_limits(**{**LIM, **lim})
+    return lib.ds_sel_check_args(ctypes.byref(limits), ctypes.byref(args))
+
+
+def test_valid_arguments_pass(lib):
+    assert check(lib, _args()) == sel.DS_SEL_OK
+    assert check(lib, _args(mask_rows=6)) == sel.DS_SEL_OK
+    assert check(lib, _args(mask_rows=0, with_limit=False)) == sel.DS_SEL_OK
+    assert check(lib, _args(N=0, keys_ptr=0)) == sel.DS_SEL_OK
+    assert check(lib, _args(d=64, H=4, ldk=72), max_dim=128) == sel.DS_SEL_OK
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("layers", 0, sel.DS_SEL_E_INVALID),
+    ("rows", 0, sel.DS_SEL_E_INVALID),
+    ("rows", 9, sel.DS_SEL_E_INVALID),
+    ("heads", 0, sel.DS_SEL_E_INVALID),
+    ("k", 0, sel.DS_SEL_E_INVALID),
+    ("k", 4096, sel.DS_SEL_E_INVALID),
+    ("blocks", -1, sel.DS_SEL_E_INVALID),
+    ("dim", 96, sel.DS_SEL_E_UNSUPPORTED),
+    ("dim", 100, sel.DS_SEL_E_INVALID),
+    ("q", None, sel.DS_SEL_E_INVALID),
+    ("out_idx", None, sel.DS_SEL_E_INVALID),
+    ("keys", None, sel.DS_SEL_E_INVALID),
+    ("keys", 0x20008, sel.DS_SEL_E_INVALID),       # not 16-byte aligned
+    ("ldk", 120, sel.DS_SEL_E_INVALID),            # ldk < d
+    ("ldk", 132, sel.DS_SEL_E_INVALID),            # ldk not a multiple of 8
+    ("key_layer_stride", 8, sel.DS_SEL_E_INVALID),  # layers overlap
+    ("mask_row_stride", 5, sel.DS_SEL_E_INVALID),   # shorter than a mask row
+    ("mask_layer_stride", 3, sel.DS_SEL_E_INVALID),
+    ("limit", 0x50002, sel.DS_SEL_E_INVALID),       # misaligned int32
+    ("struct_size", 8, sel.DS_SEL_E_INVALID),
+])
+def test_bad_arguments_rejected(lib, field, value, expect):
+    a = _args()
+    setattr(a, field, value)
+    assert check(lib, a) == expect
+
+
+@pytest.mark.parametrize("field,value", [("layers", 44), ("rows", 6), ("heads", 64), ("k", 512),
+                                         ("blocks", 75000)])
+def test_capacity_enforced(lib, field, value):
+    a = _args(L=1)
+    setattr(a, field, value + 1 if field != "rows" else 7)
+    if field == "blocks":
+        a.key_layer_stride = (value + 1) * 128
+    assert check(lib, a) == sel.DS_SEL_E_CAPACITY
+
+
+def test_bad_limits_rejected(lib):
+    for field, value in [("max_rows", 9), ("max_k", 4097), ("max_layers", 0), ("max_dim", 512),
+                         ("max_blocks", -1)]:
+        lim = sel.make_limits(**LIM)
+        setattr(lim, field, value)
+        assert lib.ds_sel_scratch_bytes(ctypes.byref(lim)) == 0
+        h = ctypes.c_void_p()
+        assert lib.ds_sel_create(ctypes.byref(lim), ctypes.byref(h)) == sel.DS_SEL_E_INVALID
+
+
+def test_scratch_bytes(lib):
+    lim = sel.make_limits(**LIM)
+    nbytes = lib.ds_sel_scratch_bytes(ctypes.byref(lim))
+    keys = 43 * 6 * 75000 * 4
+    assert keys < nbytes < keys * 1.5
+
+
+def test_no_device_or_create(lib):
+    """Without a GPU, create reports DS_SEL_E_NODEVICE and hands back no handle."""
+    lim = sel.make_limits(**LIM)
+    h = ctypes.c_void_p(1234)
+    rc = lib.ds_sel_create(ctypes.byref(lim), ctypes.byref(h))
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU driver is present on this host")
+    assert rc == sel.DS_SEL_E_NODEVICE
+    assert not h.value
+
+
+def test_destroy_null_is_noop_and_status_strings(lib):
+    lib.ds_sel_destroy(None)
+    assert lib.ds_sel_status_string(0) == b"ok"
+    assert lib.ds_sel_status_string(sel.DS_SEL_E_CAPACITY) == b"exceeds the handle's capacity"
+    assert lib.ds_sel_status_string(99) == b"unknown status"

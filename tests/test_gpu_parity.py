@@ -1,0 +1,156 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer-valued inputs must match bit for bit; general inputs follow the
+tolerance and set-acceptance rule in tests/gpu_support.py."""
+import numpy as np
+import pytest
+
+from sparse_attention_block_ds_amd import selector as sel
+from sparse_attention_block_ds_amd import workloads as wl
+from tests import gpu_support as gs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def selector():
+    import torch
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    s = sel.Selector(max_layers=43, max_rows=8, max_heads=64, max_dim=256, max_blocks=75000,
+                     max_k=2048)
+    yield s
+    s.close()
+
+
+def _print_case(name, p):
+    print(f"\n[case] {name}: L={p.layers} R={p.rows} H={p.heads} d={p.dim} N={p.blocks} k={p.k} "
+          f"mask={'none' if p.mask is None else p.mask.shape} seed={p.meta.get('seed')}", flush=True)
+
+
+# ------------------------------------------------------------ named workloads
+def test_tiny_bit_exact(selector):
+    p = wl.make("tiny")
+    _print_case("tiny", p)
+    gs.assert_bit_exact(gs.run_gpu(selector, p), gs.run_oracle(p), "tiny")
+
+
+def test_verify_int_bit_exact(selector):
+    p = wl.make("verify_int")
+    _print_case("verify_int", p)
+    gs.assert_bit_exact(gs.run_gpu(selector, p), gs.run_oracle(p), "verify_int")
+
+
+@pytest.mark.parametrize("name", ["8k", "300k", "verify"])
+def test_general_workloads(selector, name):
+    p = wl.make(name)
+    _print_case(name, p)
+    gpu = gs.run_gpu(selector, p)
+    gs.assert_self_consistent(p, gpu)
+    gs.assert_general(p, gpu, gs.run_oracle(p))
+
+
+def test_sweep_full_size_sampled(selector):
+    """All 43 x 6 selections at full size: invariants everywhere, bit-exact on a sample."""
+    p = wl.make("sweep")
+    _print_case("sweep", p)
+    gpu = gs.run_gpu(selector, p)
+    gs.assert_self_consistent(p, gpu)
+    for l, r in [(0, 0), (0, 5), (17, 3), (42, 0), (42, 5)]:
+        sub = wl.Problem("s", p.k, p.q[l:l + 1, r:r + 1], p.w[l:l + 1, r:r + 1], p.keys[l:l + 1],
+                         p.mask[l:l + 1], p.limit[l:l + 1, r:r + 1])
+        o = gs.run_oracle(sub)
+        got = tuple(x[l:l + 1, r:r + 1] for x in gpu)
+        gs.assert_bit_exact(got, o, f"sweep l={l} r={r}")
+
+
+# ------------------------------------------------------------ edge cases (integer: bit-exact)
+EDGE = [
+    dict(name="n_below_k", args=(1, 2, 8, 64, 300, 512), kw=dict(values="int3")),
+    dict(name="n_one", args=(1, 1, 8, 64, 1, 512), kw=dict(values="int3")),
+    dict(name="n_zero", args=(2, 3, 8, 64, 0, 16), kw=dict(values="int3")),
+    dict(name="ragged_shared_mask", args=(2, 3, 16, 128, 4097, 512), kw=dict(values="int3", mask_p=0.5)),
+    dict(name="empty_mask", args=(1, 2, 8, 64, 3000, 64), kw=dict(values="int3", mask_p=0.0)),
+    dict(name="limit_zero", args=(1, 3, 8, 64, 3000, 64), kw=dict(values="int3", limits=0)),
+    dict(name="limits_clamped", args=(1, 2, 8, 64, 2000, 256),
+         kw=dict(values="int3", limits=np.array([[-5, 10 ** 7]]))),
+    dict(name="all_equal_sort_path", args=(1, 2, 8, 64, 5000, 512), kw=dict(values="zero_keys")),
+    dict(name="all_equal_fallback", args=(1, 2, 8, 64, 30000, 512),
+         kw=dict(values="zero_keys", mask_p=0.9)),
+    dict(name="per_row_mask", args=(2, 6, 16, 128, 9000, 512),
+         kw=dict(values="int3", mask_p=0.3, mask_shared=False)),
+    dict(name="per_row_mask_limits", args=(1, 4, 16, 128, 5000, 300),
+         kw=dict(values="ternary", mask_p=0.6, mask_shared=False,
+                 limits=np.array([[5000, 2500, 17, 4999]]))),
+    dict(name="ldk_padded_nan", args=(1, 2, 8, 64, 3000, 128), kw=dict(values="int3", ldk=72)),
+    dict(name="dim32", args=(1, 3, 8, 32, 2500, 128), kw=dict(values="int3")),
+    dict(name="dim256", args=(1, 3, 8, 256, 2500, 128), kw=dict(values="int3")),
+    dict(name="k_one", args=(2, 3, 8, 64, 3000, 1), kw=dict(values="int3", mask_p=0.5)),
+    dict(name="k_2048", args=(1, 2, 8, 128, 6000, 2048), kw=dict(values="int3", mask_p=0.7)),
+    dict(name="heads_one", args=(1, 2, 1, 128, 3000, 64), kw=dict(values="int3")),
+    dict(name="ternary_ties", args=(3, 6, 64, 128, 20000, 512),
+         kw=dict(values="ternary", mask_p=0.5, limits=np.array([[20000 - 5 + r for r in range(6)]]))),
+] + [dict(name=f"rows{r}", args=(1, r, 8, 64, 2100, 100), kw=dict(values="int3", mask_p=0.8))
+     for r in range(1, 9)]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c["name"] for c in EDGE])
+def test_edge_cases_bit_exact(selector, case):
+    p = wl.make_custom(*case["args"], seed=100 + EDGE.index(case), **case["kw"])
+    _print_case(case["name"], p)
+    gpu = gs.run_gpu(selector, p)
+    gs.assert_self_consistent(p, gpu)
+    gs.assert_bit_exact(gpu, gs.run_oracle(p), case["name"])
+
+
+def test_fallback_with_distinct_keys(selector):
+    """More than the LDS buffer in the boundary bin, with many distinct keys and ties:
+    K[b][0] takes 128 values in [1, 2) and q~ picks only that column."""
+    rng = np.random.default_rng(7)
+    L, R, H, d, N, k = 1, 2, 2, 64, 40000, 512
+    q = np.zeros((L, R, H, d), np.float32)
+    q[:, :, 0, 0] = 1.0
+    w = np.ones((L, R, H), np.float32)
+    keys = np.zeros((L, N, d), np.float32)
+    keys[0, :, 0] = 1.0 + rng.integers(0, 128, N) / 128.0
+    p = wl.Problem("fallback", k, wl.f32_to_bf16_bits(q), wl.f32_to_bf16_bits(w),
+                   wl.f32_to_bf16_bits(keys), None, None, True)
+    _print_case("fallback_distinct", p)
+    gs.assert_bit_exact(gs.run_gpu(selector, p), gs.run_oracle(p), "fallback_distinct")
+
+
+@pytest.mark.parametrize("values,mask_p,shared", [("normal", None, True), ("normal", 0.4, True),
+                                                  ("normal", 0.5, False)])
+def test_general_custom(selector, values, mask_p, shared):
+    p = wl.make_custom(3, 6, 64, 128, 12000, 512, seed=200, values=values, mask_p=mask_p,
+                       mask_shared=shared, limits=np.array([[12000 - 5 + r for r in range(6)]]))
+    _print_case(f"general_{mask_p}_{shared}", p)
+    gpu = gs.run_gpu(selector, p)
+    gs.assert_self_consistent(p, gpu)
+    gs.assert_general(p, gpu, gs.run_oracle(p))
+
+
+def test_repeated_calls_identical(selector):
+    """Atomic append order must not leak into the output (tie-heavy input)."""
+    import torch
+    p = wl.make_custom(2, 6, 64, 128, 20000, 512, seed=300, values="ternary", mask_p=0.7)
+    q, w, keys, mask, limit = sel.upload(p)
+    first = [t.clone() for t in selector.score_select(q, w, keys, p.k, mask, limit)]
+    for _ in range(20):
+        out = selector.score_select(q, w, keys, p.k, mask, limit)
+        for a, b in zip(first, out):
+            assert torch.equal(a, b)
+    torch.cuda.synchronize()
+
+
+def test_capacity_error_leaves_outputs_untouched(selector):
+    import torch
+    p = wl.make_custom(1, 2, 8, 64, 80000, 16, seed=301, values="int3")
+    q, w, keys, mask, limit = sel.upload(p)
+    out = (torch.full((1, 2, 16), 7, dtype=torch.int32, device="cuda"),
+           torch.full((1, 2, 16), 7.0, device="cuda"),
+           torch.full((1, 2), 7, dtype=torch.int32, device="cuda"))
+    with pytest.raises(sel.DsSelError) as e:
+        selector.score_select(q, w, keys, 16, mask, limit, out=out)
+    assert e.value.status == sel.DS_SEL_E_CAPACITY
+    torch.cuda.synchronize()
+    assert all(bool((t == 7).all()) for t in out)
