@@ -53,7 +53,26 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--engine", default="mfma", choices=["mfma", "valu"],
+                    help="key-stream engine: bf16 matrix cores (default) or fp32 vector FMAs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB read + 1 GiB write elementwise kernel, to scale "
+                         "the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain elementwise kernel of known traffic: reads 1 GiB, writes 1 GiB."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel": "bitwise_not int32", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 3}), flush=True)
 
 
 def admitted_counts(p):
@@ -157,6 +176,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
     import numpy as np
     import torch
     from sparse_attention_block_ds_amd import selector as sel
@@ -177,7 +200,8 @@ def main():
     n_sets = 1 if set_bytes >= 2 * MALL_BYTES else int(np.ceil(2 * MALL_BYTES / set_bytes)) + 1
     sets = [sel.upload(p, "cuda:0") for _ in range(n_sets)]
     selector = sel.Selector(max_layers=p.layers, max_rows=p.rows, max_heads=p.heads,
-                            max_dim=p.dim, max_blocks=p.blocks, max_k=p.k, device=0)
+                            max_dim=p.dim, max_blocks=p.blocks, max_k=p.k, device=0,
+                            engine=args.engine)
     outs = [(torch.empty((p.layers, p.rows, p.k), dtype=torch.int32, device="cuda:0"),
              torch.empty((p.layers, p.rows, p.k), dtype=torch.float32, device="cuda:0"),
              torch.empty((p.layers, p.rows), dtype=torch.int32, device="cuda:0"))
@@ -258,7 +282,7 @@ def main():
             }[p.name],
             "layers": p.layers, "rows": p.rows, "heads": p.heads, "dim": p.dim,
             "blocks": p.blocks, "k": p.k, "candidates_per_step": candidates,
-            "input_sets_rotated": n_sets,
+            "input_sets_rotated": n_sets, "engine": args.engine,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

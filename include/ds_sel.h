@@ -70,6 +70,13 @@ enum {
 #define DS_SEL_MAX_DIM 256
 #define DS_SEL_MAX_BLOCKS (1LL << 26)
 
+/* Create-time flags.  The default key-stream engine feeds the bf16 keys to the
+ * matrix cores (the fp32 folded query enters as three exact bf16 parts);
+ * DS_SEL_FLAG_VALU_SCORE selects fp32 FMAs on the vector ALUs instead.  Both
+ * return the same selection on integer-valued inputs; on general inputs their
+ * scores differ only by fp32 rounding order. */
+#define DS_SEL_FLAG_VALU_SCORE 1u
+
 typedef struct ds_sel ds_sel; /* opaque handle; owns device scratch */
 
 /* Create-time capacity.  Every call on the handle must fit inside it. */
@@ -81,7 +88,7 @@ typedef struct {
   int32_t max_heads;    /* 1 .. DS_SEL_MAX_HEADS */
   int32_t max_dim;      /* 1 .. DS_SEL_MAX_DIM */
   int32_t max_k;        /* 1 .. DS_SEL_MAX_K */
-  int32_t reserved;     /* must be 0 */
+  int32_t flags;        /* 0, or DS_SEL_FLAG_* bits */
   int64_t max_blocks;   /* 0 .. DS_SEL_MAX_BLOCKS */
 } ds_sel_limits;
 

@@ -25,7 +25,7 @@ SOURCES = ["ds_sel.cpp", "prep.hip", "score.hip", "select.hip"]
 
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-pass-failed",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -26,6 +26,22 @@ __device__ __forceinline__ float key_to_score(uint32_t key) {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Round a finite fp32 value to bf16, nearest with ties to even.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Bits of mask word j (blocks 32j .. 32j+31) that lie below `lim`.
+__device__ __forceinline__ uint32_t below_limit_bits(int64_t j, int64_t lim) {
+  const int64_t lo = j * 32;
+  if (lim >= lo + 32) return 0xFFFFFFFFu;
+  if (lim <= lo) return 0u;
+  return (1u << (uint32_t)(lim - lo)) - 1u;
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Inclusive prefix sum across the 64 lanes of a wave.

@@ -13,7 +13,8 @@ struct ds_sel {
   void* scratch = nullptr;
   int64_t scratch_bytes = 0;
   // offsets into scratch
-  int64_t off_qt = 0, off_list = 0, off_counts = 0, off_keys = 0, off_hist = 0;
+  int64_t off_qt = 0, off_qparts = 0, off_tiles = 0, off_list = 0, off_counts = 0, off_keys = 0,
+          off_hist = 0;
 };
 
 namespace {
@@ -23,19 +24,23 @@ constexpr int64_t kAlign = 256;
 int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  int64_t qt, list, counts, keys, hist, total;
+  int64_t qt, qparts, tiles, list, counts, keys, hist, total;
 };
 
-// Scratch for a capacity: q~ fp32 [L][R][d], index int32 [L][N], counts
-// int32 [L][9], radix keys uint32 [L][R][N], histograms uint32 [L][R][2048].
+// Scratch for a capacity: q~ fp32 [L][R][d] and its bf16 parts [L][3][R][d],
+// tile directory int32 [L][tiles+1], index int32 [L][N], counts int32 [L][9],
+// radix keys uint32 [L][R][N], histograms uint32 [L][R][2048].
 Layout layout_for(const ds_sel_limits& lim) {
   Layout s{};
   const int64_t L = lim.max_layers, R = lim.max_rows, D = lim.max_dim, N = lim.max_blocks;
+  const int64_t tiles = (N + dssel::kTileBlocks - 1) / dssel::kTileBlocks;
   int64_t off = 0;
   s.qt = off;     off += align_up(L * R * D * 4);
+  s.qparts = off; off += align_up(L * 3 * R * D * 2);
+  s.tiles = off;  off += align_up(L * (tiles + 1) * 4);
   s.list = off;   off += align_up(L * N * 4);
   s.counts = off; off += align_up(L * dssel::kCountStride * 4);
-  s.keys = off;   off += align_up(L * R * N * 4);
+  s.keys = off;   off += align_up(L * R * ((N + 3) / 4 * 4) * 4);
   s.hist = off;   off += align_up(L * R * dssel::kHistBins * 4);
   s.total = off;
   return s;
@@ -49,7 +54,7 @@ int check_limits(const ds_sel_limits* lim) {
   if (lim->max_dim < 1 || lim->max_dim > DS_SEL_MAX_DIM) return DS_SEL_E_INVALID;
   if (lim->max_k < 1 || lim->max_k > DS_SEL_MAX_K) return DS_SEL_E_INVALID;
   if (lim->max_blocks < 0 || lim->max_blocks > DS_SEL_MAX_BLOCKS) return DS_SEL_E_INVALID;
-  if (lim->reserved != 0 || lim->device < 0) return DS_SEL_E_INVALID;
+  if ((lim->flags & ~DS_SEL_FLAG_VALU_SCORE) != 0 || lim->device < 0) return DS_SEL_E_INVALID;
   return DS_SEL_OK;
 }
 
@@ -159,6 +164,8 @@ int ds_sel_create(const ds_sel_limits* lim, ds_sel** out) {
   }
   h->scratch_bytes = s.total;
   h->off_qt = s.qt;
+  h->off_qparts = s.qparts;
+  h->off_tiles = s.tiles;
   h->off_list = s.list;
   h->off_counts = s.counts;
   h->off_keys = s.keys;
@@ -220,11 +227,23 @@ int enqueue(ds_sel* h, const ds_sel_args* a, void* hip_stream, void* const* even
   c.mode = !a->mask ? dssel::kNoMask
                     : ((a->mask_row_stride == 0 || a->rows == 1) ? dssel::kSharedMask
                                                                  : dssel::kRowMask);
+  c.engine = (h->lim.flags & DS_SEL_FLAG_VALU_SCORE) ? dssel::kEngineValu : dssel::kEngineMfma;
+  c.ntiles = (int32_t)((a->blocks + dssel::kTileBlocks - 1) / dssel::kTileBlocks);
+  c.key_row = (a->blocks + 3) / 4 * 4;
+  {
+    const int64_t full = (int64_t)a->layers * a->blocks;  // admitted positions at most
+    int64_t piece = (full + dssel::kScoreTargetWgs - 1) / dssel::kScoreTargetWgs;
+    piece = (piece + 63) / 64 * 64;
+    piece = piece < dssel::kScorePieceMin ? dssel::kScorePieceMin : piece;
+    c.piece = (int32_t)(piece > dssel::kScorePieceMax ? dssel::kScorePieceMax : piece);
+  }
   c.out_idx = a->out_idx;
   c.out_score = a->out_score;
   c.out_count = a->out_count;
   char* base = static_cast<char*>(h->scratch);
   c.qt = reinterpret_cast<float*>(base + h->off_qt);
+  c.qparts = reinterpret_cast<uint16_t*>(base + h->off_qparts);
+  c.tile_off = reinterpret_cast<int32_t*>(base + h->off_tiles);
   c.list = reinterpret_cast<int32_t*>(base + h->off_list);
   c.counts = reinterpret_cast<int32_t*>(base + h->off_counts);
   c.skeys = reinterpret_cast<uint32_t*>(base + h->off_keys);

@@ -19,12 +19,17 @@ constexpr int kDigit3Bins = 1 << 10;
 constexpr int kMaxRows = 8;
 constexpr int kCountStride = kMaxRows + 1;   // per layer: n_r for r < 8, union size at [8]
 
-constexpr int kPrepThreads = 512;
-constexpr int kPrepWordsPerThread = 8;
+// The block axis is cut into tiles of 2048 blocks (64 mask words).  prep
+// counts each tile's admitted blocks and turns the counts into the tile's
+// first compacted position; the score kernel compacts one tile per workgroup.
+constexpr int kTileBlocks = 2048;
+constexpr int kTileWords = kTileBlocks / 32;
 
+constexpr int kPrepThreads = 1024;
 constexpr int kScoreThreads = 256;           // 4 waves
-constexpr int kScoreChunk = 2048;            // union positions per score workgroup
-
+constexpr int kScorePieceMax = 2048;         // admitted positions per score workgroup: at most,
+constexpr int kScorePieceMin = 64;           // at least, and about (L * N) / kScoreTargetWgs
+constexpr int kScoreTargetWgs = 1024;        // four resident workgroups per compute unit
 constexpr int kSelectThreads = 1024;         // 16 waves
 constexpr int kSelectBuf = 8192;             // LDS (key, position) slots for the select
 
@@ -34,11 +39,19 @@ enum AdmitMode : int {
   kRowMask = 2,     // a mask row per query row: one union list, per-row sentinels
 };
 
+enum Engine : int {
+  kEngineMfma = 0,  // bf16 matrix cores on an exact 3-way bf16 split of the fp32 q~
+  kEngineValu = 1,  // fp32 FMAs on the vector ALUs
+};
+
 // Everything one call needs, in element units, passed by value to kernels.
 struct Call {
   int32_t layers, rows, heads, dim, k;
-  int32_t mode;
+  int32_t mode, engine;
+  int32_t ntiles;     // ceil(N / kTileBlocks)
+  int32_t piece;      // admitted positions per score workgroup
   int64_t blocks;
+  int64_t key_row;    // stride of a row of radix keys: N rounded up to 4 (16 bytes)
   const uint16_t* q;
   const uint16_t* w;
   const uint16_t* keys;
@@ -50,10 +63,12 @@ struct Call {
   float* out_score;
   int32_t* out_count;
   // scratch (owned by the handle), laid out with this call's dimensions
-  float* qt;          // [L][R][d] folded query rows
+  float* qt;          // [L][R][d] folded query rows, fp32
+  uint16_t* qparts;   // [L][3][R][d] bf16 hi/mid/lo parts of q~ (hi + mid + lo == q~)
+  int32_t* tile_off;  // [L][ntiles + 1] first compacted position of each tile
   int32_t* list;      // [L][N] compacted admitted (union) index, ascending
   int32_t* counts;    // [L][kCountStride]
-  uint32_t* skeys;    // [L][R][N] radix keys at compacted positions
+  uint32_t* skeys;    // [L][R][key_row] radix keys at compacted positions
   uint32_t* hist;     // [L][R][kHistBins] first-digit histograms
 };
 

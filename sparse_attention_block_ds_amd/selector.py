@@ -22,6 +22,7 @@ DS_SEL_E_NODEVICE = 3
 DS_SEL_E_HIP = 4
 DS_SEL_E_NOMEM = 5
 DS_SEL_E_UNSUPPORTED = 6
+DS_SEL_FLAG_VALU_SCORE = 1
 
 EXPORTED = ("ds_sel_create", "ds_sel_score_select", "ds_sel_score_select_profiled",
             "ds_sel_destroy", "ds_sel_check_args", "ds_sel_scratch_bytes", "ds_sel_status_string")
@@ -31,7 +32,7 @@ class Limits(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("device", ctypes.c_int32),
                 ("max_layers", ctypes.c_int32), ("max_rows", ctypes.c_int32),
                 ("max_heads", ctypes.c_int32), ("max_dim", ctypes.c_int32),
-                ("max_k", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_k", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("max_blocks", ctypes.c_int64)]
 
 
@@ -56,10 +57,12 @@ class DsSelError(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIBRARY):
-    """Load libdssel.so; raises if it has not been built."""
+def load_library(path: Optional[str] = None):
+    """Load libdssel.so (or the library at `path`); raises if it has not been built."""
     global _lib
-    if _lib is not None and path == LIBRARY:
+    default = path is None
+    path = LIBRARY if default else path
+    if _lib is not None and default:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
@@ -81,7 +84,7 @@ def load_library(path: str = LIBRARY):
     lib.ds_sel_scratch_bytes.restype = ctypes.c_int64
     lib.ds_sel_status_string.argtypes = [ctypes.c_int]
     lib.ds_sel_status_string.restype = ctypes.c_char_p
-    if path == LIBRARY:
+    if default:
         _lib = lib
     return lib
 
@@ -93,9 +96,10 @@ def status_string(status: int) -> str:
         return "status"
 
 
-def make_limits(max_layers, max_rows, max_heads, max_dim, max_blocks, max_k=512, device=0):
+def make_limits(max_layers, max_rows, max_heads, max_dim, max_blocks, max_k=512, device=0,
+                flags=0):
     return Limits(ctypes.sizeof(Limits), device, max_layers, max_rows, max_heads, max_dim, max_k,
-                  0, max_blocks)
+                  flags, max_blocks)
 
 
 def _ptr(t):
@@ -126,13 +130,15 @@ class Selector:
     """One libdssel handle: scratch sized for the given capacity on one device."""
 
     def __init__(self, max_layers, max_rows, max_heads, max_dim, max_blocks, max_k=512,
-                 device: Optional[int] = None):
+                 device: Optional[int] = None, engine: str = "mfma"):
         import torch
         self._torch = torch
         self.lib = load_library()
         self.device = torch.cuda.current_device() if device is None else device
+        if engine not in ("mfma", "valu"):
+            raise ValueError("engine must be 'mfma' or 'valu'")
         self.limits = make_limits(max_layers, max_rows, max_heads, max_dim, max_blocks, max_k,
-                                  self.device)
+                                  self.device, DS_SEL_FLAG_VALU_SCORE if engine == "valu" else 0)
         h = ctypes.c_void_p()
         rc = self.lib.ds_sel_create(ctypes.byref(self.limits), ctypes.byref(h))
         if rc != DS_SEL_OK:
@@ -173,6 +179,9 @@ class Selector:
         if events is None:
             rc = self.lib.ds_sel_score_select(self.handle, ctypes.byref(a), ctypes.c_void_p(handle))
         else:
+            for e in events:  # torch creates the HIP event on its first record
+                if not e.cuda_event:
+                    e.record(stream)
             ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
             rc = self.lib.ds_sel_score_select_profiled(self.handle, ctypes.byref(a),
                                                        ctypes.c_void_p(handle), ev)

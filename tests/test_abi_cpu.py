@@ -163,7 +163,7 @@ def test_capacity_enforced(lib, field, value):
 
 
 def test_bad_limits_rejected(lib):
-    for field, value in [("max_rows", 9), ("max_k", 4097), ("max_layers", 0), ("max_dim", 512),
+    for field, value in [("max_rows", 9), ("max_k", 4097), ("max_layers", 0), ("max_dim", 512), ("flags", 2),
                          ("max_blocks", -1)]:
         lim = sel.make_limits(**LIM)
         setattr(lim, field, value)

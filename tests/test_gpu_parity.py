@@ -12,12 +12,12 @@ from tests import gpu_support as gs
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def selector():
+@pytest.fixture(scope="module", params=["mfma", "valu"])
+def selector(request):
     import torch
     assert torch.cuda.is_available(), "the gpu tests need a GPU"
     s = sel.Selector(max_layers=43, max_rows=8, max_heads=64, max_dim=256, max_blocks=75000,
-                     max_k=2048)
+                     max_k=2048, engine=request.param)
     yield s
     s.close()
 
