@@ -102,7 +102,7 @@ typedef struct {
   int32_t dim;          /* d in {32, 64, 128, 256} */
   int32_t k;            /* 1 .. max_k; k > #admitted is allowed (padding) */
   int64_t blocks;       /* N >= 0 */
-  const void* q;        /* bf16 [L][R][H][d], contiguous */
+  const void* q;        /* bf16 [L][R][H][d], contiguous, 16-byte aligned */
   const void* w;        /* bf16 [L][R][H], contiguous */
   const void* keys;     /* bf16; block b of layer l at keys + l*key_layer_stride + b*ldk;
                            16-byte aligned; may be NULL only when N == 0 */
@@ -155,7 +155,12 @@ void ds_sel_destroy(ds_sel* h);
 int ds_sel_check_args(const ds_sel_limits* lim, const ds_sel_args* a);
 
 /* Bytes of device scratch a handle with capacity `lim` allocates (0 on a bad
- * capacity). */
+ * capacity).  With L, R, D, N the capacity's layers, rows, dim and blocks and
+ * each part rounded up to 256 bytes: the folded query (L R D fp32), its three
+ * bf16 parts (3 L R D), the compacted admitted index (L N int32), per-layer
+ * counts (9 L int32), candidate floors (L R uint32), candidate counters one
+ * per 128 bytes (32 L R int32), and candidate lists with room for every
+ * position (L R ceil4(N) uint64). */
 int64_t ds_sel_scratch_bytes(const ds_sel_limits* lim);
 
 /* A static string naming a status code. */

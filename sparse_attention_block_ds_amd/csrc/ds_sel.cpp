@@ -12,9 +12,10 @@ struct ds_sel {
   ds_sel_limits lim;
   void* scratch = nullptr;
   int64_t scratch_bytes = 0;
+  int compute_units = 256;  // of the handle's device, read at create
   // offsets into scratch
-  int64_t off_qt = 0, off_qparts = 0, off_tiles = 0, off_list = 0, off_counts = 0, off_keys = 0,
-          off_hist = 0;
+  int64_t off_qt = 0, off_qparts = 0, off_list = 0, off_counts = 0, off_floor = 0, off_ccount = 0,
+          off_cand = 0;
 };
 
 namespace {
@@ -24,24 +25,24 @@ constexpr int64_t kAlign = 256;
 int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  int64_t qt, qparts, tiles, list, counts, keys, hist, total;
+  int64_t qt, qparts, list, counts, floor, ccount, cand, total;
 };
 
 // Scratch for a capacity: q~ fp32 [L][R][d] and its bf16 parts [L][3][R][d],
-// tile directory int32 [L][tiles+1], index int32 [L][N], counts int32 [L][9],
-// radix keys uint32 [L][R][N], histograms uint32 [L][R][2048].
+// compacted index int32 [L][N], counts int32 [L][9], candidate floors uint32
+// [L][R], candidate counts int32 [L][R] (one per 128 bytes), and candidate words uint64
+// [L][R][N rounded up to 4] (room for every position, so none is ever dropped).
 Layout layout_for(const ds_sel_limits& lim) {
   Layout s{};
   const int64_t L = lim.max_layers, R = lim.max_rows, D = lim.max_dim, N = lim.max_blocks;
-  const int64_t tiles = (N + dssel::kTileBlocks - 1) / dssel::kTileBlocks;
   int64_t off = 0;
   s.qt = off;     off += align_up(L * R * D * 4);
   s.qparts = off; off += align_up(L * 3 * R * D * 2);
-  s.tiles = off;  off += align_up(L * (tiles + 1) * 4);
   s.list = off;   off += align_up(L * N * 4);
   s.counts = off; off += align_up(L * dssel::kCountStride * 4);
-  s.keys = off;   off += align_up(L * R * ((N + 3) / 4 * 4) * 4);
-  s.hist = off;   off += align_up(L * R * dssel::kHistBins * 4);
+  s.floor = off;  off += align_up(L * R * 4);
+  s.ccount = off; off += align_up(L * R * dssel::kCountPad * 4);
+  s.cand = off;   off += align_up(L * R * ((N + 3) / 4 * 4) * 8);
   s.total = off;
   return s;
 }
@@ -75,7 +76,7 @@ int check_args(const ds_sel_limits& lim, const ds_sel_args* a) {
       a->dim > lim.max_dim || a->k > lim.max_k || a->blocks > lim.max_blocks)
     return DS_SEL_E_CAPACITY;
   if (!a->q || !a->w || !a->out_idx || !a->out_score) return DS_SEL_E_INVALID;
-  if (!aligned(a->q, 2) || !aligned(a->w, 2) || !aligned(a->out_idx, 4) ||
+  if (!aligned(a->q, 16) || !aligned(a->w, 2) || !aligned(a->out_idx, 4) ||
       !aligned(a->out_score, 4) || !aligned(a->out_count, 4) || !aligned(a->limit, 4) ||
       !aligned(a->mask, 4))
     return DS_SEL_E_INVALID;
@@ -151,6 +152,11 @@ int ds_sel_create(const ds_sel_limits* lim, ds_sel** out) {
   h->lim = *lim;
   const Layout s = layout_for(*lim);
   rc = with_device(lim->device, [&]() {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, lim->device) == hipSuccess &&
+        cus > 0)
+      h->compute_units = cus;
+    (void)hipGetLastError();
     if (hipMalloc(&h->scratch, (size_t)s.total) != hipSuccess) {
       (void)hipGetLastError();
       h->scratch = nullptr;
@@ -165,11 +171,11 @@ int ds_sel_create(const ds_sel_limits* lim, ds_sel** out) {
   h->scratch_bytes = s.total;
   h->off_qt = s.qt;
   h->off_qparts = s.qparts;
-  h->off_tiles = s.tiles;
   h->off_list = s.list;
   h->off_counts = s.counts;
-  h->off_keys = s.keys;
-  h->off_hist = s.hist;
+  h->off_floor = s.floor;
+  h->off_ccount = s.ccount;
+  h->off_cand = s.cand;
   *out = h;
   return DS_SEL_OK;
 }
@@ -229,13 +235,16 @@ int enqueue(ds_sel* h, const ds_sel_args* a, void* hip_stream, void* const* even
                                                                  : dssel::kRowMask);
   c.engine = (h->lim.flags & DS_SEL_FLAG_VALU_SCORE) ? dssel::kEngineValu : dssel::kEngineMfma;
   c.ntiles = (int32_t)((a->blocks + dssel::kTileBlocks - 1) / dssel::kTileBlocks);
-  c.key_row = (a->blocks + 3) / 4 * 4;
+  c.cand_stride = (a->blocks + 3) / 4 * 4;
   {
-    const int64_t full = (int64_t)a->layers * a->blocks;  // admitted positions at most
-    int64_t piece = (full + dssel::kScoreTargetWgs - 1) / dssel::kScoreTargetWgs;
-    piece = (piece + 63) / 64 * 64;
-    piece = piece < dssel::kScorePieceMin ? dssel::kScorePieceMin : piece;
-    c.piece = (int32_t)(piece > dssel::kScorePieceMax ? dssel::kScorePieceMax : piece);
+    // Score grid: every resident slot (four workgroups per compute unit), and
+    // enough workgroups that a piece never exceeds kScorePieceMax positions
+    // even when every block is admitted.
+    const int64_t slots = (int64_t)dssel::kScoreWgsPerCu * h->compute_units;
+    const int64_t need = a->layers + ((int64_t)a->layers * a->blocks + dssel::kScorePieceMax - 1) /
+                                         dssel::kScorePieceMax;
+    c.score_slots = (int32_t)slots;
+    c.score_wgs = (int32_t)(slots > need ? slots : need);
   }
   c.out_idx = a->out_idx;
   c.out_score = a->out_score;
@@ -243,11 +252,11 @@ int enqueue(ds_sel* h, const ds_sel_args* a, void* hip_stream, void* const* even
   char* base = static_cast<char*>(h->scratch);
   c.qt = reinterpret_cast<float*>(base + h->off_qt);
   c.qparts = reinterpret_cast<uint16_t*>(base + h->off_qparts);
-  c.tile_off = reinterpret_cast<int32_t*>(base + h->off_tiles);
   c.list = reinterpret_cast<int32_t*>(base + h->off_list);
   c.counts = reinterpret_cast<int32_t*>(base + h->off_counts);
-  c.skeys = reinterpret_cast<uint32_t*>(base + h->off_keys);
-  c.hist = reinterpret_cast<uint32_t*>(base + h->off_hist);
+  c.floor_key = reinterpret_cast<uint32_t*>(base + h->off_floor);
+  c.cand_count = reinterpret_cast<int32_t*>(base + h->off_ccount);
+  c.cand = reinterpret_cast<uint64_t*>(base + h->off_cand);
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   auto mark = [&](int i) {

@@ -19,24 +19,30 @@ constexpr int kDigit3Bins = 1 << 10;
 constexpr int kMaxRows = 8;
 constexpr int kCountStride = kMaxRows + 1;   // per layer: n_r for r < 8, union size at [8]
 
-// The block axis is cut into tiles of 2048 blocks (64 mask words).  prep
-// counts each tile's admitted blocks and turns the counts into the tile's
-// first compacted position; the score kernel compacts one tile per workgroup.
+// The block axis is cut into tiles of 2048 blocks (64 mask words); one wave
+// expands one tile of the compacted admitted index.
 constexpr int kTileBlocks = 2048;
 constexpr int kTileWords = kTileBlocks / 32;
 
-constexpr int kPrepThreads = 1024;
+constexpr int kPrepThreads = 1024;                  // 16 waves
+constexpr int kPrepTilesPerWg = kPrepThreads / 64;  // tiles expanded per prep workgroup
+constexpr int kSampleSlots = 512;                   // blocks per layer scored to place the floors
+
 constexpr int kScoreThreads = 256;           // 4 waves
 constexpr int kScorePieceMax = 2048;         // admitted positions per score workgroup: at most,
-constexpr int kScorePieceMin = 64;           // at least, and about (L * N) / kScoreTargetWgs
-constexpr int kScoreTargetWgs = 1024;        // four resident workgroups per compute unit
+constexpr int kScorePieceMin = 64;           // and at least
+constexpr int kScoreWgsPerCu = 4;            // resident score workgroups per compute unit
+constexpr int kWaveCandBuf = 128;            // per-wave, per-row candidate staging (LDS)
+constexpr int kCountPad = 32;                // candidate counters sit 128 bytes apart
+
 constexpr int kSelectThreads = 1024;         // 16 waves
-constexpr int kSelectBuf = 8192;             // LDS (key, position) slots for the select
+constexpr int kSelectBuf = 8192;             // LDS candidate slots; also the most held in registers
+constexpr int kGatherMin = 1024;             // radix passes stop once this many words remain
 
 enum AdmitMode : int {
   kNoMask = 0,      // admitted = b < limit: the compacted index is the identity
   kSharedMask = 1,  // one mask row per layer: every row's list is a prefix of one list
-  kRowMask = 2,     // a mask row per query row: one union list, per-row sentinels
+  kRowMask = 2,     // a mask row per query row: one union list, per-row admission
 };
 
 enum Engine : int {
@@ -49,9 +55,10 @@ struct Call {
   int32_t layers, rows, heads, dim, k;
   int32_t mode, engine;
   int32_t ntiles;     // ceil(N / kTileBlocks)
-  int32_t piece;      // admitted positions per score workgroup
+  int32_t score_wgs;    // score grid: >= layers + ceil(L * N / kScorePieceMax)
+  int32_t score_slots;  // resident score workgroups on the device
   int64_t blocks;
-  int64_t key_row;    // stride of a row of radix keys: N rounded up to 4 (16 bytes)
+  int64_t cand_stride;  // candidate slots per (layer, row): N rounded up to 4
   const uint16_t* q;
   const uint16_t* w;
   const uint16_t* keys;
@@ -63,13 +70,13 @@ struct Call {
   float* out_score;
   int32_t* out_count;
   // scratch (owned by the handle), laid out with this call's dimensions
-  float* qt;          // [L][R][d] folded query rows, fp32
-  uint16_t* qparts;   // [L][3][R][d] bf16 hi/mid/lo parts of q~ (hi + mid + lo == q~)
-  int32_t* tile_off;  // [L][ntiles + 1] first compacted position of each tile
-  int32_t* list;      // [L][N] compacted admitted (union) index, ascending
-  int32_t* counts;    // [L][kCountStride]
-  uint32_t* skeys;    // [L][R][key_row] radix keys at compacted positions
-  uint32_t* hist;     // [L][R][kHistBins] first-digit histograms
+  float* qt;           // [L][R][d] folded query rows, fp32
+  uint16_t* qparts;    // [L][3][R][d] bf16 hi/mid/lo parts of q~ (hi + mid + lo == q~)
+  int32_t* list;       // [L][N] compacted admitted (union) index, ascending
+  int32_t* counts;     // [L][kCountStride]
+  uint32_t* floor_key; // [L][R] candidate floor: keys below it cannot be in the top k
+  int32_t* cand_count; // [L][R][kCountPad] candidates appended (element 0 of each line)
+  uint64_t* cand;      // [L][R][cand_stride] (key << 32) | ~position, unordered
 };
 
 hipError_t launch_prep(const Call& c, hipStream_t stream);

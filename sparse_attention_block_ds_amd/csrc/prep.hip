@@ -1,27 +1,38 @@
-// prep: the admission directory, the head-weight fold, and clearing of the
-// first-digit histograms, for every layer of one call.
+// prep: per layer, the admitted counts, the compacted admitted index, the
+// head-weight fold and the candidate floors.
 //
-// Admission directory (page "DeepSeek V4.1F Q4 on M3 Ultra with native DSpark
-// MTP (40tps / 800tps)", paragraph "Decode at depth": the admitted index is
-// compacted once per row).  The block axis is cut into tiles of 2048 blocks
-// (64 mask words).  One workgroup per layer reads the mask words coalesced,
-// one wave per tile: each lane ANDs its word with the causal limits and
-// popcounts it, a wave prefix sum places the word inside its tile, a workgroup
-// prefix sum over the tiles places the tile, and each lane writes its word's
-// admitted block indices at their compacted positions: the compacted index is
-// built in one pass, in ascending order.  When all rows share one mask row, the
-// rows' lists are prefixes of one list (they differ only by their limits): each
-// row keeps only its length.  Without a mask the compacted index is the
-// identity and nothing is built.
+// Admission and compaction (page "DeepSeek V4.1F Q4 on M3 Ultra with native
+// DSpark MTP (40tps / 800tps)", paragraph "Decode at depth": only blocks the
+// mask admits are scored, and the admitted index is compacted once per row).
+// A block is admitted for row r if its mask bit is set (when there is a mask)
+// and it lies below the row's causal limit.  The layer's union over rows is
+// compacted into one ascending index; when all rows share one mask row, each
+// row's own list is a prefix of it (the rows differ only by their limits), so
+// only the row's length is kept.  Without a mask the index is the identity and
+// nothing is built.  The block axis is cut into tiles of 2048 blocks (64 mask
+// words); workgroup x >= 1 of a layer expands tiles [16 (x-1), 16 x): it first
+// counts the admitted blocks of all earlier tiles (a workgroup sum over their
+// mask words), then each wave takes one tile: a wave prefix sum over its
+// words' popcounts places every admitted block, the wave writes them into LDS
+// in order and copies the tile's run to the global index in coalesced stores.
 //
-// Fold: score = sum_h w_h (q_h . K_b) = (sum_h w_h q_h) . K_b, so each row's
-// H query heads collapse into one fp32 vector q~ before the key stream.  The
-// products w_h q_hi are bf16 x bf16 and exact in fp32.  Thread (g, i) of the
-// fold workgroup sums head group g of column i in ascending h, and the groups
-// are added in a fixed tree, so the result is the same on every run.  For the
-// matrix cores q~ is also split exactly into three bf16 parts, hi = bf16(q~),
-// mid = bf16(q~ - hi), lo = bf16(q~ - hi - mid), with hi + mid + lo == q~
-// (each step keeps 8 more significant bits of the 24).
+// Fold (workgroup 0 of each layer): score = sum_h w_h (q_h . K_b) =
+// (sum_h w_h q_h) . K_b, so each row's H query heads collapse into one fp32
+// vector q~ before the key stream (the products w_h q_hi are bf16 x bf16 and
+// exact in fp32; the sum runs in ascending h).  For the matrix cores q~ is
+// also split exactly into three bf16 parts, hi = bf16(q~), mid = bf16(q~ - hi),
+// lo = bf16(q~ - hi - mid), with hi + mid + lo == q~.
+//
+// Candidate floors (workgroup 0): the key stream writes only keys that can
+// still be among a row's best k, i.e. keys at or above the row's floor.  The
+// floor comes from 512 blocks spread evenly over the layer: their keys are
+// sorted per row, and the floor is the sample key about three times more
+// selective than k would suggest (rank 3 k n_sample / n_admitted, plus 8).
+// Any floor is safe: the candidate lists have room for every position, and
+// the select rescores the row exactly when fewer than min(k, admitted)
+// candidates came through.  The floor only decides how few keys are written;
+// at 512 samples and 75000 admitted blocks the expected sample count above the
+// k-th key is 3.5 and the rank taken is 19, so a rescore is a ~1e-8 event.
 #include "device_util.h"
 #include "dssel_internal.h"
 
@@ -32,7 +43,7 @@ constexpr int kPrepWaves = kPrepThreads / kWave;
 
 __device__ __forceinline__ int64_t clamp_limit(const int32_t* limit, int64_t idx, int64_t n) {
   if (!limit) return n;
-  int64_t v = limit[idx];
+  const int64_t v = limit[idx];
   return v < 0 ? 0 : (v > n ? n : v);
 }
 
@@ -42,147 +53,365 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-__device__ void tile_directory(const Call& c, int l) {
-  __shared__ int scan_scratch[kPrepWaves + 1];
-  __shared__ int tile_cnt[kPrepWaves];
-  __shared__ int row_totals[kMaxRows];
-  const int R = c.rows;
-  const int64_t N = c.blocks;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-
+struct Limits {
   int64_t lim[kMaxRows];
-  int64_t maxlim = 0;
+  int64_t maxlim;
+};
+
+__device__ __forceinline__ Limits layer_limits(const Call& c, int l) {
+  Limits s;
+  s.maxlim = 0;
 #pragma unroll
   for (int r = 0; r < kMaxRows; ++r) {
-    lim[r] = r < R ? clamp_limit(c.limit, (int64_t)l * R + r, N) : 0;
-    maxlim = lim[r] > maxlim ? lim[r] : maxlim;
+    s.lim[r] = r < c.rows ? clamp_limit(c.limit, (int64_t)l * c.rows + r, c.blocks) : 0;
+    s.maxlim = s.lim[r] > s.maxlim ? s.lim[r] : s.maxlim;
   }
-  int32_t* counts = c.counts + (int64_t)l * kCountStride;
-  if (c.mode == kNoMask) {
-#pragma unroll
-    for (int r = 0; r < kMaxRows; ++r)
-      if (tid == r && r < R) counts[r] = (int32_t)lim[r];
-    if (tid == 0) counts[kMaxRows] = (int32_t)maxlim;
-    return;
-  }
+  return s;
+}
 
-  if (tid < kMaxRows) row_totals[tid] = 0;
-  const int64_t words = (maxlim + 31) / 32;
-  const uint32_t* mrow0 = c.mask + (int64_t)l * c.mask_layer_stride;
-  int32_t* tile_off = c.tile_off + (int64_t)l * (c.ntiles + 1);
-  int32_t* list = c.list + (int64_t)l * N;
-  int row_count[kMaxRows];
+// Union of the rows' admitted blocks in mask word j (blocks 32 j .. 32 j + 31).
+__device__ __forceinline__ uint32_t union_word(const Call& c, const uint32_t* mask_l, const Limits& s,
+                                               int64_t j) {
+  if (c.mode == kSharedMask) return mask_l[j] & below_limit_bits(j, s.maxlim);
+  uint32_t u = 0;
 #pragma unroll
-  for (int r = 0; r < kMaxRows; ++r) row_count[r] = 0;
+  for (int r = 0; r < kMaxRows; ++r)
+    if (r < c.rows) u |= mask_l[r * c.mask_row_stride + j] & below_limit_bits(j, s.lim[r]);
+  return u;
+}
 
-  int base = 0;
-  // kPrepWaves tiles per pass: wave w takes tile t0 + w, lane = its word
-  for (int t0 = 0; t0 < c.ntiles; t0 += kPrepWaves) {
-    const int t = t0 + wave;
-    const int64_t j = (int64_t)t * kTileWords + lane;
-    uint32_t u = 0;
-    if (t < c.ntiles && j < words) {
-      if (c.mode == kSharedMask) {
-        u = mrow0[j] & below_limit_bits(j, maxlim);
+// Row r's admitted blocks in mask word j.
+__device__ __forceinline__ uint32_t row_word(const Call& c, const uint32_t* mask_l, const Limits& s,
+                                             int r, int64_t j) {
+  const uint32_t m = c.mode == kSharedMask ? mask_l[j] : mask_l[r * c.mask_row_stride + j];
+  return m & below_limit_bits(j, s.lim[r]);
+}
+
+// LDS of the fold workgroup and of the expanding workgroups (never both).
+struct FoldShared {
+  float part[kPrepThreads * 8];            // fold partial sums, [head slice][r * d + i]
+  float q[kMaxRows][256];                  // folded query rows
+  uint32_t skey[kMaxRows][kSampleSlots];   // sample keys (0: not admitted by the row)
+  int64_t lim[kMaxRows];                   // the rows' limits, clamped to [0, N]
+  int acc[kMaxRows + 1];
+};
+
+struct ExpandShared {
+  int32_t stage[kPrepWaves][kTileBlocks];  // one tile's compacted run per wave
+  int tile_cnt[kPrepWaves];
+  int scan[kPrepWaves + 1];
+  int before;
+};
+
+union PrepShared {
+  FoldShared f;
+  ExpandShared e;
+};
+
+// Block of sample slot j: (2 j + 1) * maxlim / (2 S) with S = min(512, maxlim),
+// i.e. the middle of the j-th of S equal stretches of [0, maxlim).
+__device__ __forceinline__ int64_t sample_block(int j, int64_t maxlim) {
+  return maxlim >= kSampleSlots ? ((2 * (int64_t)j + 1) * maxlim) >> 10 : j;
+}
+static_assert(kSampleSlots == 512, "sample_block divides by 2 * 512 with a shift");
+
+// The sample slots one thread serves: d/8 lanes share a sampled block, each
+// holding 16 bytes of its key row and, for the rows it writes (r % (d/8) ==
+// its slice), the mask word of the block.
+template <int R, int NP>
+struct SampleLoads {
+  static constexpr int kRowsPerLane = 2;  // d = 32: 4 lanes per block, up to 8 rows
+  uint4 k[NP];
+  uint32_t mw[NP][kRowsPerLane];
+
+  __device__ void issue(const Call& c, int l, int64_t maxlim, const uint32_t* mask_l, int p0,
+                        int passes, int S) {
+    const int LPR = c.dim / 8, per_pass = kPrepThreads / LPR;
+    const int slice = threadIdx.x % LPR, sub = threadIdx.x / LPR;
+    const uint16_t* K = c.keys + (int64_t)l * c.key_layer_stride;
 #pragma unroll
-        for (int r = 0; r < kMaxRows; ++r)
-          if (r < R) row_count[r] += __popc(u & below_limit_bits(j, lim[r]));
-      } else {
+    for (int u = 0; u < NP; ++u) {
+      const int j = (p0 + u) * per_pass + sub;
+      k[u] = uint4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int r = 0; r < kMaxRows; ++r) {
-          if (r < R) {
-            const uint32_t mr = mrow0[r * c.mask_row_stride + j] & below_limit_bits(j, lim[r]);
-            row_count[r] += __popc(mr);
-            u |= mr;
+      for (int i = 0; i < kRowsPerLane; ++i) mw[u][i] = 0xFFFFFFFFu;
+      if (p0 + u < passes && j < S) {
+        const int64_t b = sample_block(j, maxlim);
+        k[u] = *reinterpret_cast<const uint4*>(K + b * c.ldk + slice * 8);
+        if (c.mode == kSharedMask) {
+          mw[u][0] = mw[u][1] = mask_l[b >> 5];
+        } else if (c.mode == kRowMask) {
+#pragma unroll
+          for (int i = 0; i < kRowsPerLane; ++i) {
+            const int r = slice + i * LPR;
+            if (r < R) mw[u][i] = mask_l[r * c.mask_row_stride + (b >> 5)];
           }
         }
       }
     }
-    const int cnt = __popc(u);
-    const int in_tile = wave_inclusive_scan(cnt) - cnt;  // this word's offset in its tile
-    if (lane == kWave - 1) tile_cnt[wave] = in_tile + cnt;
-    __syncthreads();
-    int total = 0;
-    const int mine = tid < kPrepWaves ? tile_cnt[tid] : 0;
-    const int excl = block_exclusive_scan<kPrepThreads>(mine, &total, scan_scratch);
-    if (tid < kPrepWaves) tile_cnt[tid] = excl;  // tile offsets within this pass
-    if (tid < kPrepWaves && t0 + tid < c.ntiles) tile_off[t0 + tid] = base + excl;
-    __syncthreads();
-    // expand the word's admitted blocks at their compacted positions, in order
-    int pos = base + tile_cnt[wave] + in_tile;
-    const int32_t b0 = (int32_t)(j * 32);
-    while (u) {
-      list[pos++] = b0 + (__ffs(u) - 1);
-      u &= u - 1u;
-    }
-    base += total;
-    __syncthreads();
   }
+
+  // Dot the held rows with q~ and store the admitted rows' keys.
+  __device__ void finish(const Call& c, int64_t maxlim, int p0, int passes, int S,
+                         const float (&qv)[R][8], FoldShared& sh) {
+    const int LPR = c.dim / 8, per_pass = kPrepThreads / LPR;
+    const int slice = threadIdx.x % LPR, sub = threadIdx.x / LPR;
 #pragma unroll
-  for (int r = 0; r < kMaxRows; ++r) {
-    const int v = wave_sum(row_count[r]);
-    if (r < R && lane == 0 && v) atomicAdd(&row_totals[r], v);
+    for (int u = 0; u < NP; ++u) {
+      const int j = (p0 + u) * per_pass + sub;
+      const uint32_t k4[4] = {k[u].x, k[u].y, k[u].z, k[u].w};
+      float d[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        d[r] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          d[r] = fmaf(qv[r][2 * e], bf16_lo(k4[e]), d[r]);
+          d[r] = fmaf(qv[r][2 * e + 1], bf16_hi(k4[e]), d[r]);
+        }
+      }
+      for (int m = 1; m < LPR; m <<= 1)
+#pragma unroll
+        for (int r = 0; r < R; ++r) d[r] += __shfl_xor(d[r], m, kWave);
+      if (p0 + u < passes && j < S) {
+        const int64_t b = sample_block(j, maxlim);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r % LPR != slice) continue;
+          const uint32_t w = r < LPR ? mw[u][0] : mw[u][1];
+          if (b < sh.lim[r] && ((w >> (b & 31)) & 1u)) sh.skey[r][j] = score_to_key(d[r]);
+        }
+      }
+    }
   }
-  __syncthreads();
-  if (tid < R) counts[tid] = row_totals[tid];
-  if (tid == 0) {
-    counts[kMaxRows] = base;
-    tile_off[c.ntiles] = base;
+};
+
+// The j-th largest of the 512 keys a wave holds (8 per lane): the largest x
+// with at least j keys >= x, built bit by bit from the top.
+__device__ __forceinline__ uint32_t wave_jth_largest(const uint32_t (&v)[kSampleSlots / kWave], int j) {
+  uint32_t x = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t t = x | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < kSampleSlots / kWave; ++i) n += __popcll(__ballot(v[i] >= t));
+    if (n >= j) x = t;
   }
+  return x;
 }
 
-__device__ void fold_row(const Call& c, int l, int r) {
-  __shared__ float partial[kPrepThreads];
-  const int H = c.heads, D = c.dim, R = c.rows;
-  const int groups = kPrepThreads / D;          // 4 .. 32 head groups
-  const int per = (H + groups - 1) / groups;
-  const int i = threadIdx.x % D, g = threadIdx.x / D;
-  const int64_t lr = (int64_t)l * R + r;
-  const uint16_t* qrow = c.q + lr * H * D;
-  const uint16_t* wrow = c.w + lr * H;
-  const int h0 = g * per, h1 = h0 + per < H ? h0 + per : H;
-  float acc = 0.0f;
-#pragma unroll 8
-  for (int h = h0; h < h1; ++h)
-    acc = fmaf(bf16_to_f32(wrow[h]), bf16_to_f32(qrow[(int64_t)h * D + i]), acc);
-  partial[threadIdx.x] = acc;
-  __syncthreads();
-  // fixed pairwise tree over the head groups
-  for (int s = groups / 2; s > 0; s >>= 1) {
-    if (g < s) partial[threadIdx.x] = partial[threadIdx.x] + partial[threadIdx.x + s * D];
-    __syncthreads();
+// Workgroup 0 of layer l: counts, fold, floors.  Every global load the
+// workgroup needs (sampled key rows and their mask words, the query heads and
+// weights, the mask words to count) is issued before any of them is used.
+template <int R>
+__device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
+  constexpr int NP = R <= 6 ? 8 : 4;  // sample passes in flight
+  const int D = c.dim, H = c.heads;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const Limits s = layer_limits(c, l);
+  const uint32_t* mask_l = c.mask ? c.mask + (int64_t)l * c.mask_layer_stride : nullptr;
+  int32_t* counts = c.counts + (int64_t)l * kCountStride;
+
+  if (tid <= kMaxRows) sh.acc[tid] = 0;
+  if (tid < kMaxRows) sh.lim[tid] = tid < R ? clamp_limit(c.limit, (int64_t)l * R + tid, c.blocks) : 0;
+  for (int i = tid; i < kMaxRows * kSampleSlots; i += kPrepThreads) (&sh.skey[0][0])[i] = 0u;
+
+  // sampled key rows (the first NP passes)
+  const int S = s.maxlim < kSampleSlots ? (int)s.maxlim : kSampleSlots;
+  const int passes = (S * (D / 8) + kPrepThreads - 1) / kPrepThreads;
+  SampleLoads<R, NP> smp;
+  smp.issue(c, l, s.maxlim, mask_l, 0, passes, S);
+
+  // fold, first half: thread (slice hs, chunk) sums w_h q_h[i0 .. i0 + 8) over
+  // its slice of heads, ascending h, eight heads' loads at a time
+  const int chunks = R * D / 8;
+  const int slices = kPrepThreads / chunks;  // >= 4
+  const int hper = (H + slices - 1) / slices;
+  if (tid < chunks * slices) {
+    const int ch = tid % chunks, hs = tid / chunks;
+    const int r = ch / (D / 8), i0 = (ch % (D / 8)) * 8;
+    const int64_t lr = (int64_t)l * R + r;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    const int h0 = hs * hper, h1 = h0 + hper < H ? h0 + hper : H;
+    for (int hb = h0; hb < h1; hb += 8) {
+      uint4 qv[8];
+      float wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int h = hb + u < h1 ? hb + u : h1 - 1;  // repeated loads past h1 are not summed
+        qv[u] = *reinterpret_cast<const uint4*>(c.q + (lr * H + h) * D + i0);
+        wv[u] = bf16_to_f32(c.w[lr * H + h]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (hb + u >= h1) break;
+        const uint32_t q4[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(wv[u], bf16_lo(q4[e]), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(wv[u], bf16_hi(q4[e]), acc[2 * e + 1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sh.part[hs * R * D + r * D + i0 + e] = acc[e];
   }
-  if (g == 0) {
-    const float q = partial[i];
-    c.qt[lr * D + i] = q;
-    const uint16_t hi = f32_to_bf16_rne(q);
-    const float r1 = q - bf16_to_f32(hi);   // exact: q minus its own rounding
+
+  // admitted counts per row and for the union
+  __syncthreads();
+  if (c.mode == kNoMask) {
+    if (tid < R) sh.acc[tid] = (int)sh.lim[tid];
+    if (tid == 0) sh.acc[kMaxRows] = (int)s.maxlim;
+  } else {
+    const int64_t words = (s.maxlim + 31) / 32;
+    int rc[kMaxRows + 1];
+#pragma unroll
+    for (int r = 0; r <= kMaxRows; ++r) rc[r] = 0;
+    for (int64_t j = tid; j < words; j += kPrepThreads) {
+      rc[kMaxRows] += __popc(union_word(c, mask_l, s, j));
+#pragma unroll
+      for (int r = 0; r < R; ++r) rc[r] += __popc(row_word(c, mask_l, s, r, j));
+    }
+#pragma unroll
+    for (int r = 0; r <= kMaxRows; ++r) {
+      if (r < R || r == kMaxRows) {
+        const int v = wave_sum(rc[r]);
+        if (lane == 0 && v) atomicAdd(&sh.acc[r], v);
+      }
+    }
+  }
+
+  // fold, second half: the slices' partial sums in ascending slice order; the
+  // exact three-way bf16 split
+  for (int o = tid; o < R * D; o += kPrepThreads) {
+    const int r = o / D, i = o % D;
+    const int64_t lr = (int64_t)l * R + r;
+    float acc = 0.0f;
+    for (int hs = 0; hs < slices; ++hs) acc += sh.part[hs * R * D + o];
+    sh.q[r][i] = acc;
+    c.qt[lr * D + i] = acc;
+    const uint16_t hi = f32_to_bf16_rne(acc);
+    const float r1 = acc - bf16_to_f32(hi);   // exact: acc minus its own rounding
     const uint16_t mid = f32_to_bf16_rne(r1);
-    const float r2 = r1 - bf16_to_f32(mid);  // exact for the same reason
+    const float r2 = r1 - bf16_to_f32(mid);   // exact for the same reason
     const uint16_t lo = f32_to_bf16_rne(r2);
     uint16_t* parts = c.qparts + ((int64_t)l * 3 * R + r) * D + i;
     parts[0] = hi;
     parts[(int64_t)R * D] = mid;
     parts[(int64_t)2 * R * D] = lo;
   }
+  __syncthreads();
+  if (tid <= kMaxRows && (tid < R || tid == kMaxRows)) counts[tid] = sh.acc[tid];
+
+  // sample keys
+  {
+    const int slice = tid % (D / 8);
+    float qv[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[r][e] = sh.q[r][slice * 8 + e];
+    smp.finish(c, s.maxlim, 0, passes, S, qv, sh);
+    for (int p0 = NP; p0 < passes; p0 += NP) {  // d = 256: the rest of the passes
+      smp.issue(c, l, s.maxlim, mask_l, p0, passes, S);
+      smp.finish(c, s.maxlim, p0, passes, S, qv, sh);
+    }
+  }
+  __syncthreads();
+
+  // floors: wave r finds row r's jth largest sample key
+  if (wave < R) {
+    const int r = wave;
+    uint32_t v[kSampleSlots / kWave];
+    int sr = 0;  // admitted samples: the non-zero keys
+#pragma unroll
+    for (int i = 0; i < kSampleSlots / kWave; ++i) {
+      v[i] = sh.skey[r][i * kWave + lane];
+      sr += __popcll(__ballot(v[i] != 0u));
+    }
+    const int64_t n = sh.acc[r];
+    const int64_t m = n < c.k ? n : c.k;
+    uint32_t floor = 0;
+    if (sr > 0 && n > 3 * m) {
+      const int64_t jth = (3 * m * sr + n - 1) / n + 8;
+      if (jth <= sr) floor = wave_jth_largest(v, (int)jth);
+    }
+    if (lane == 0) {
+      c.floor_key[(int64_t)l * R + r] = floor;
+      c.cand_count[((int64_t)l * R + r) * kCountPad] = 0;
+    }
+  }
 }
 
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(Call c) {
-  const int l = blockIdx.y;
-  if (blockIdx.x == 0) {
-    uint32_t* h = c.hist + (int64_t)l * c.rows * kHistBins;
-    for (int i = threadIdx.x; i < c.rows * kHistBins; i += kPrepThreads) h[i] = 0u;
-    tile_directory(c, l);
-  } else {
-    fold_row(c, l, blockIdx.x - 1);
+// Workgroup x >= 1 of layer l: expand tiles [16 (x-1), 16 x) of the union.
+__device__ void expand_tiles(const Call& c, int l, int x, ExpandShared& sh) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const Limits s = layer_limits(c, l);
+  const uint32_t* mask_l = c.mask + (int64_t)l * c.mask_layer_stride;
+  const int64_t words = (s.maxlim + 31) / 32;
+  const int t0 = (x - 1) * kPrepTilesPerWg;
+
+  // this wave's tile word (loaded alongside the earlier tiles' words)
+  const int t = t0 + wave;
+  const int64_t j = (int64_t)t * kTileWords + lane;
+  const uint32_t u = (t < c.ntiles && j < words) ? union_word(c, mask_l, s, j) : 0u;
+
+  // admitted blocks of all earlier tiles
+  int before = 0;
+  const int64_t w_end = (int64_t)t0 * kTileWords < words ? (int64_t)t0 * kTileWords : words;
+  for (int64_t jj = tid; jj < w_end; jj += kPrepThreads) before += __popc(union_word(c, mask_l, s, jj));
+  if (tid == 0) sh.before = 0;
+  __syncthreads();
+  before = wave_sum(before);
+  if (lane == 0 && before) atomicAdd(&sh.before, before);
+
+  // place the tile's admitted blocks in order: lane i's k-th set bit goes to
+  // its exclusive prefix + k.  Each lane walks its 32 bits starting at bit
+  // i % 32, so at every step the lanes write to different LDS banks.
+  const int cnt = __popc(u);
+  const int in_tile = wave_inclusive_scan(cnt) - cnt;
+  const int tile_total = __shfl(in_tile + cnt, kWave - 1, kWave);
+  if (lane == 0) sh.tile_cnt[wave] = tile_total;
+  const int32_t b0 = (int32_t)(j * 32);
+  for (int step = 0; step < 32; ++step) {
+    const int bit = (step + lane) & 31;
+    if ((u >> bit) & 1u) sh.stage[wave][in_tile + __popc(u & ((1u << bit) - 1u))] = b0 + bit;
   }
+  __syncthreads();
+  int total = 0;
+  const int mine = tid < kPrepWaves ? sh.tile_cnt[tid] : 0;
+  const int excl = block_exclusive_scan<kPrepThreads>(mine, &total, sh.scan);
+  if (tid < kPrepWaves) sh.tile_cnt[tid] = excl;
+  __syncthreads();
+  int32_t* out = c.list + (int64_t)l * c.blocks + sh.before + sh.tile_cnt[wave];
+  for (int i = lane; i < tile_total; i += kWave) out[i] = sh.stage[wave][i];
+}
+
+template <int R>
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(Call c) {
+  __shared__ PrepShared sh;
+  if (blockIdx.x == 0) fold_count_floor<R>(c, blockIdx.y, sh.f);
+  else expand_tiles(c, blockIdx.y, blockIdx.x, sh.e);
 }
 
 }  // namespace
 
 hipError_t launch_prep(const Call& c, hipStream_t stream) {
-  dim3 grid(1 + c.rows, c.layers);
-  hipLaunchKernelGGL(prep_kernel, grid, dim3(kPrepThreads), 0, stream, c);
+  const int expanders = c.mode == kNoMask ? 0 : (c.ntiles + kPrepTilesPerWg - 1) / kPrepTilesPerWg;
+  dim3 grid(1 + expanders, c.layers);
+  switch (c.rows) {
+    case 1: hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 2: hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 3: hipLaunchKernelGGL(prep_kernel<3>, grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 5: hipLaunchKernelGGL(prep_kernel<5>, grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 6: hipLaunchKernelGGL(prep_kernel<6>, grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 7: hipLaunchKernelGGL(prep_kernel<7>, grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 8: hipLaunchKernelGGL(prep_kernel<8>, grid, dim3(kPrepThreads), 0, stream, c); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

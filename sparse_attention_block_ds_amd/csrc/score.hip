@@ -1,22 +1,22 @@
-// score: the compacted admitted index and one pass over the admitted block
-// keys shared by all query rows of a layer, writing the rows' order-preserving
-// radix keys at the compacted positions and counting their first radix digit.
+// score: one pass over the admitted block keys shared by all query rows of a
+// layer; every (row, block) score at or above the row's candidate floor leaves
+// as a (key, position) candidate.
 //
 // Page "DeepSeek V4.1F Q4 on M3 Ultra with native DSpark MTP (40tps /
-// 800tps)": paragraph "Decode at depth" -- only admitted blocks are scored,
-// and the admitted index is compacted once per row; paragraph "DSpark" -- the
-// rows of a speculative verify share one stream of data, here the key stream:
-// each admitted K row is read from HBM once and dotted with every row's query.
+// 800tps)": paragraph "Decode at depth" -- only admitted blocks are scored;
+// paragraph "DSpark" -- the rows of a speculative verify share one stream of
+// data, here the key stream: each admitted K row is read from HBM once and
+// dotted with every row's query.
 //
-// Work split: workgroup (l, j) takes positions [j * piece, (j + 1) * piece) of
-// layer l's compacted admitted index, so the workgroups stream equal numbers of
-// key rows whatever the masks look like (`piece` is chosen on the host so that
-// a full-size call fills the chip with one round of resident workgroups, and a
-// single layer still spreads over hundreds of them); workgroups past a layer's
-// admitted positions exit at once.  A workgroup:
-//  1. Set-up, one round of independent loads: the layer's counts and limits,
-//     the piece's slice of the compacted index (built by prep) into LDS, and
-//     the folded query.
+// Work split: the admitted positions of all layers are cut into equal pieces
+// sized on the device from the admitted totals, so that one launch fills every
+// resident slot (four workgroups per compute unit) and each workgroup streams
+// the same number of key rows whatever the masks look like; a piece lies in
+// one layer.  A workgroup:
+//  0. Finds its piece from the per-layer admitted counts (wave 0).
+//  1. Set-up, one round of independent loads: the layer's counts, limits and
+//     floors, the piece's slice of the compacted index (built by prep) into
+//     LDS, and the folded query.
 //  2. Key stream: each wave takes 16 consecutive compacted entries at a time
 //     and loads their K rows with 16-byte loads (each instruction reads 16 rows
 //     x 64 contiguous bytes), two steps ahead of the arithmetic.
@@ -26,9 +26,12 @@
 //       matrix cores directly: no vector-ALU conversion, no cross-lane sum.
 //       VALU engine: d/8 lanes per key row, 8 fp32 FMAs per lane and row, a
 //       butterfly across the row's lanes.
-//  3. Epilogue per (row, entry): radix key -> keys[l][r][pos]; the first digit
-//     is counted in an LDS histogram (two 16-bit counters per word), added to
-//     the layer's global histogram at the end.
+//  3. Epilogue: the score becomes an order-preserving radix key; keys at or
+//     above the row's floor are staged per wave and row in LDS and flushed to
+//     the row's candidate list with one global atomic per flush.  Nothing is
+//     written for the other keys: writing every key would add one write for
+//     every 10 to 64 bytes read, and writes mixed into the read stream cost
+//     the stream far more than their size.
 #include "device_util.h"
 #include "dssel_internal.h"
 
@@ -41,44 +44,93 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 16;                     // compacted entries per wave step
 constexpr int kWaves = kScoreThreads / kWave;  // 4
-constexpr int kPiece = kScorePieceMax;         // largest piece one workgroup compacts and streams
+constexpr int kPiece = kScorePieceMax;         // largest piece one workgroup streams
 
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+__device__ __forceinline__ uint64_t pack_candidate(uint32_t key, int pos) {
+  return ((uint64_t)key << 32) | (uint32_t)~(uint32_t)pos;
+}
+
+template <int R>
+struct ScoreShared {
+  int32_t list[kPiece];
+  uint64_t stage[kWaves][R][kWaveCandBuf];
+  int P[kMaxRows];
+  int64_t lim[kMaxRows];
+  uint32_t floor[kMaxRows];
+  int piece[3];
+  int wstaged[kWaves][kMaxRows];  // end of piece: each wave's staged count per row
+  int base[kMaxRows];             // end of piece: the workgroup's slot in each row's list
+};
+
+// A wave's n staged candidates of one row go to the row's list, at a slot
+// taken with one atomic.  It runs once per kWaveCandBuf candidates of a wave
+// and row: a cold path, laid out away from the stream loop.
+__device__ __forceinline__ void flush_staged(const uint64_t* stage, int n, int32_t* counter,
+                                                       uint64_t* list, int64_t stride) {
+  int base = 0;
+  if (lane_id() == 0) base = atomicAdd(counter, n);
+  base = __shfl(base, 0, kWave);
+  wave_lds_sync();
+  for (int i = lane_id(); i < n; i += kWave)
+    if (base + i < stride) list[base + i] = stage[i];
+  wave_lds_sync();
+}
+
+// Per-wave candidate staging and the piece's context.
 template <int R>
 struct PieceCtx {
-  int64_t key_row;
   int off, cnt;                // positions [off, off + cnt) of the current layer
   int mode;
-  const int32_t* sh_list;      // block index of each entry of the piece
-  const int* sh_P;             // positions [0, P[r]) hold row r's keys
-  const int64_t* sh_lim;       // clamped causal limits of the layer's rows
-  uint32_t* sh_hist;           // [R][kHistBins / 2], two 16-bit counters per word
-  uint32_t* skeys_l;           // keys of this layer: [R][key_row]
+  const ScoreShared<R>* sh;
+  uint64_t* stage;             // this wave's [R][kWaveCandBuf]
+  int staged[R];               // per row, the same in every lane of the wave
+  int32_t* cand_count;         // [R][kCountPad] of this layer
+  uint64_t* cand;              // [R][stride] of this layer
+  int64_t stride;
   const uint32_t* mask_l;      // the layer's mask rows (kRowMask)
   int64_t mask_row_stride;
 
-  // Finish one (row, entry): key to HBM, first digit to the LDS histogram.
-  __device__ __forceinline__ void emit(int r, int e, float s) const {
-    const int pos = off + e;
-    if (pos >= sh_P[r]) return;
-    bool admitted = true;
-    if (mode == kRowMask) {  // the union list also holds blocks other rows admit
-      const int b = sh_list[e];
-      const uint32_t word = mask_l[r * mask_row_stride + (b >> 5)];
-      admitted = ((word >> (b & 31)) & 1u) && (int64_t)b < sh_lim[r];
-    }
-    const uint32_t key = admitted ? score_to_key(s) : 0u;
-    skeys_l[(int64_t)r * key_row + pos] = key;
-    if (admitted)
-      atomicAdd(&sh_hist[r * (kHistBins / 2) + (key >> (kDigit1Shift + 1))],
-                1u << (16u * ((key >> kDigit1Shift) & 1u)));
+  __device__ __forceinline__ int block_of(int e) const {
+    return mode == kNoMask ? off + e : sh->list[e];
   }
 
-  __device__ __forceinline__ int block_of(int e) const {
-    return mode == kNoMask ? off + e : sh_list[e];
+  // Is position off + e a candidate of row r with score s?  Sets its key.
+  __device__ __forceinline__ bool want(int r, int e, float s, uint32_t* key) const {
+    const int pos = off + e;
+    if (e >= cnt || pos >= sh->P[r]) return false;
+    if (mode == kRowMask) {  // the union list also holds blocks other rows admit
+      const int b = sh->list[e];
+      const uint32_t word = mask_l[r * mask_row_stride + (b >> 5)];
+      if (!((word >> (b & 31)) & 1u) || (int64_t)b >= sh->lim[r]) return false;
+    }
+    *key = score_to_key(s);
+    return *key >= sh->floor[r];
+  }
+
+  // Copy row r's staged candidates to its global list (whole wave).  Only
+  // taken when a wave's staging for a row fills up.
+  __device__ __forceinline__ void flush(int r) {
+    flush_staged(stage + r * kWaveCandBuf, staged[r], cand_count + r * kCountPad, cand + r * stride,
+                 stride);
+    staged[r] = 0;
+  }
+
+  // Append the lanes' candidates of row r; called by every lane of the wave.
+  __device__ __forceinline__ void append(int r, bool ok, uint32_t key, int e) {
+    const uint64_t bal = __ballot(ok);
+    if (bal == 0) return;
+    const int n = __popcll(bal);
+    if (__builtin_expect(staged[r] + n > kWaveCandBuf, 0)) flush(r);
+    if (ok) {
+      const int lane = lane_id();
+      const uint64_t below = lane == 0 ? 0ull : (bal & (~0ull >> (kWave - lane)));
+      stage[r * kWaveCandBuf + staged[r] + __popcll(below)] = pack_candidate(key, off + e);
+    }
+    staged[r] += n;
   }
 };
 
@@ -127,7 +179,7 @@ struct MfmaEngine {
   }
 
   template <int B>
-  __device__ __forceinline__ void compute_emit(const PieceCtx<R>& t, int g0) {
+  __device__ __forceinline__ void compute_emit(PieceCtx<R>& t, int g0) {
     f32x4_t acc[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -138,12 +190,15 @@ struct MfmaEngine {
             a[s][cc], __builtin_bit_cast(bf16x8_t, buf[B][cc]), acc[s], 0, 0, 0);
     }
     const int lane = lane_id();
-    const int e = g0 + (lane & 15);
-    if (e >= t.cnt) return;
+    const int e = g0 + (lane & 15), g = lane >> 4;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const int r = 4 * s + (lane >> 4);
-      if (r < R) t.emit(r, e, (acc[s][0] + acc[s][1]) + acc[s][2]);
+      uint32_t key = 0;
+      const int r = 4 * s + g;
+      const bool ok = r < R && t.want(r, e, (acc[s][0] + acc[s][1]) + acc[s][2], &key);
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        if (4 * s + gg < R) t.append(4 * s + gg, ok && g == gg, key, e);
     }
   }
 };
@@ -181,7 +236,7 @@ struct ValuEngine {
   }
 
   template <int B>
-  __device__ __forceinline__ void compute_emit(const PieceCtx<R>& t, int g0) {
+  __device__ __forceinline__ void compute_emit(PieceCtx<R>& t, int g0) {
     const int lane = lane_id();
     const int slice = lane % LPR, rr = lane / LPR;
 #pragma unroll
@@ -204,10 +259,11 @@ struct ValuEngine {
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] += __shfl_xor(acc[r], m, kWave);
       const int e = g0 + u * RPI + rr;
-      if (e < t.cnt) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (r % LPR == slice) t.emit(r, e, acc[r]);
+      for (int r = 0; r < R; ++r) {
+        uint32_t key = 0;
+        const bool ok = r % LPR == slice && t.want(r, e, acc[r], &key);
+        t.append(r, ok, key, e);
       }
     }
   }
@@ -217,7 +273,7 @@ struct ValuEngine {
 // buffers: the loads for group j + NBUF - 1 are issued before group j is
 // computed, so NBUF - 1 groups of key rows are in flight behind the arithmetic.
 template <int NBUF, class Engine, int J>
-__device__ __forceinline__ void ring_step(Engine& eng, const PieceCtx<Engine::kRows>& pc,
+__device__ __forceinline__ void ring_step(Engine& eng, PieceCtx<Engine::kRows>& pc,
                                           const uint16_t* K, int64_t ldk, int g, int step) {
   if constexpr (J < NBUF) {
     const int gj = g + J * step;
@@ -230,7 +286,7 @@ __device__ __forceinline__ void ring_step(Engine& eng, const PieceCtx<Engine::kR
 }
 
 template <int NBUF, class Engine, int J>
-__device__ __forceinline__ void ring_prologue(Engine& eng, const PieceCtx<Engine::kRows>& pc,
+__device__ __forceinline__ void ring_prologue(Engine& eng, PieceCtx<Engine::kRows>& pc,
                                               const uint16_t* K, int64_t ldk, int g0, int step) {
   if constexpr (J < NBUF - 1) {
     const int gj = g0 + J * step;
@@ -240,86 +296,135 @@ __device__ __forceinline__ void ring_prologue(Engine& eng, const PieceCtx<Engine
 }
 
 template <int NBUF, class Engine>
-__device__ __forceinline__ void stream_piece(Engine& eng, const PieceCtx<Engine::kRows>& pc,
+__device__ __forceinline__ void stream_piece(Engine& eng, PieceCtx<Engine::kRows>& pc,
                                              const uint16_t* K, int64_t ldk, int g0, int step) {
   ring_prologue<NBUF, Engine, 0>(eng, pc, K, ldk, g0, step);
   for (int g = g0; g < pc.cnt; g += NBUF * step) ring_step<NBUF, Engine, 0>(eng, pc, K, ldk, g, step);
 }
 
-// Everything a workgroup keeps in LDS.
-template <int R>
-struct ScoreShared {
-  int32_t list[kPiece];
-  uint32_t hist[R * (kHistBins / 2)];
-  int P[kMaxRows];
-  int64_t lim[kMaxRows];
+// Which piece this workgroup streams.  Every layer's admitted positions are
+// cut into pieces of T positions, where T = ceil(total / (slots - L)) clamped
+// to [64, 2048], total is the admitted count summed over layers and slots the
+// resident workgroups of the device; the layers' pieces are numbered in layer
+// order and workgroup j takes piece j.  There are at most total / T + L pieces:
+// no more than the slots unless T had to be clamped to 2048, and never more
+// than the grid, which the host sizes for full admission at T = 2048.  So a
+// usual call runs as one round of equal workgroups, and surplus ones exit.
+struct Piece {
+  int layer, s0, s1;  // positions [s0, s1) of the layer; layer < 0: nothing to do
 };
 
-template <int R>
-__device__ void flush_hist(ScoreShared<R>& sh, uint32_t* gh) {
-  __syncthreads();
-  for (int i = threadIdx.x; i < R * (kHistBins / 2); i += kScoreThreads) {
-    const uint32_t v = sh.hist[i];
-    if (v & 0xFFFFu) atomicAdd(&gh[2 * i], v & 0xFFFFu);
-    if (v >> 16) atomicAdd(&gh[2 * i + 1], v >> 16);
-    sh.hist[i] = 0u;
+__device__ Piece find_piece(const Call& c, int* shared_out) {
+  const int lane = lane_id();
+  if (threadIdx.x < kWave) {
+    const int L = c.layers;
+    int64_t total = 0;
+    for (int l0 = 0; l0 < L; l0 += kWave) {
+      const int l = l0 + lane;
+      int64_t n = l < L ? c.counts[(int64_t)l * kCountStride + kMaxRows] : 0;
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) n += __shfl_xor(n, off, kWave);
+      total += n;
+    }
+    const int64_t div = (int64_t)c.score_slots - L;
+    const int64_t per = div > 0 ? (total + div - 1) / div : kScorePieceMax;
+    const int T = (int)(per < kScorePieceMin ? kScorePieceMin : (per > kScorePieceMax ? kScorePieceMax : per));
+    const int j = blockIdx.x;
+    int base = 0, layer = -1, s0 = 0, nl = 0;
+    for (int l0 = 0; l0 < L && layer < 0; l0 += kWave) {
+      const int l = l0 + lane;
+      const int n = l < L ? c.counts[(int64_t)l * kCountStride + kMaxRows] : 0;
+      const int g = (n + T - 1) / T;
+      const int incl = wave_inclusive_scan(g);
+      const bool mine = j >= base + incl - g && j < base + incl;
+      const uint64_t hit = __ballot(mine);
+      if (hit) {
+        const int src = __ffsll((long long)hit) - 1;
+        layer = l0 + src;
+        s0 = (j - (base + __shfl(incl - g, src, kWave))) * T;
+        nl = __shfl(n, src, kWave);
+      }
+      base += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+      shared_out[0] = layer;
+      shared_out[1] = s0;
+      shared_out[2] = layer < 0 ? 0 : (s0 + T < nl ? s0 + T : nl);
+    }
   }
   __syncthreads();
+  return Piece{shared_out[0], shared_out[1], shared_out[2]};
 }
 
 template <int R, int D, class Engine>
 __device__ __forceinline__ void score_body(const Call& c) {
   __shared__ ScoreShared<R> sh;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid / kWave;
   const int64_t N = c.blocks;
-  const int PS = c.piece;
-  const int pieces_per_layer = (int)((N + PS - 1) / PS);
-  const int sl = blockIdx.x / pieces_per_layer;
-  const int s0 = (blockIdx.x % pieces_per_layer) * PS;
+  const Piece pz = find_piece(c, sh.piece);
+  if (pz.layer < 0) return;  // uniform for the workgroup
+  const int sl = pz.layer, s0 = pz.s0, s1 = pz.s1;
 
-  // Set-up: one round of independent loads -- the layer's counts and limits,
-  // this piece's slice of the compacted index, and (in the engine) q~.
+  // Set-up: one round of independent loads.
   const int32_t* counts = c.counts + (int64_t)sl * kCountStride;
   const int nl = counts[kMaxRows];
-  if (s0 >= nl) return;  // past the layer's admitted positions: uniform for the workgroup
-  const int s1 = s0 + PS < nl ? s0 + PS : nl;
   if (c.mode != kNoMask) {
     const int32_t* list = c.list + (int64_t)sl * N + s0;
     for (int i = tid; i < s1 - s0; i += kScoreThreads) sh.list[i] = list[i];
   }
-  for (int i = tid; i < R * (kHistBins / 2); i += kScoreThreads) sh.hist[i] = 0u;
-  if (tid < kMaxRows) sh.P[tid] = tid < R ? (c.mode == kRowMask ? nl : counts[tid]) : 0;
-  if (tid < R) {
-    const int64_t v = c.limit ? (int64_t)c.limit[(int64_t)sl * R + tid] : N;
+  if (tid < kMaxRows) {
+    sh.P[tid] = tid < R ? (c.mode == kRowMask ? nl : counts[tid]) : 0;
+    sh.floor[tid] = tid < R ? c.floor_key[(int64_t)sl * R + tid] : 0u;
+    const int64_t v = (c.limit && tid < R) ? (int64_t)c.limit[(int64_t)sl * R + tid] : N;
     sh.lim[tid] = v < 0 ? 0 : (v > N ? N : v);
   }
   Engine eng;
   eng.init(c, sl);
   __syncthreads();
 
-  // The key stream over positions [s0, s1).
   PieceCtx<R> pc;
-  pc.key_row = c.key_row;
   pc.off = s0;
   pc.cnt = s1 - s0;
   pc.mode = c.mode;
-  pc.sh_list = sh.list;
-  pc.sh_P = sh.P;
-  pc.sh_lim = sh.lim;
-  pc.sh_hist = sh.hist;
-  pc.skeys_l = c.skeys + (int64_t)sl * R * c.key_row;
+  pc.sh = &sh;
+  pc.stage = &sh.stage[wave][0][0];
+#pragma unroll
+  for (int r = 0; r < R; ++r) pc.staged[r] = 0;
+  pc.cand_count = c.cand_count + (int64_t)sl * R * kCountPad;
+  pc.cand = c.cand + (int64_t)sl * R * c.cand_stride;
+  pc.stride = c.cand_stride;
   pc.mask_l = c.mask ? c.mask + (int64_t)sl * c.mask_layer_stride : nullptr;
   pc.mask_row_stride = c.mask_row_stride;
   stream_piece<Engine::kBuffers>(eng, pc, c.keys + (int64_t)sl * c.key_layer_stride, c.ldk,
-                                 (tid / kWave) * kGroup, kWaves * kGroup);
-
-  // This piece's first digits into the layer's histogram.
-  flush_hist<R>(sh, c.hist + (int64_t)sl * R * kHistBins);
+                                 wave * kGroup, kWaves * kGroup);
+  // End of the piece: one counter update per row for the whole workgroup.
+  const int lane = lane_id();
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) sh.wstaged[wave][r] = pc.staged[r];
+  }
+  __syncthreads();
+  if (tid < R) {
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) n += sh.wstaged[w][tid];
+    sh.base[tid] = n ? atomicAdd(&pc.cand_count[tid * kCountPad], n) : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int off = sh.base[r];
+    for (int w = 0; w < wave; ++w) off += sh.wstaged[w][r];
+    const uint64_t* st = pc.stage + r * kWaveCandBuf;
+    for (int i = lane; i < pc.staged[r]; i += kWave)
+      if (off + i < pc.stride) pc.cand[r * pc.stride + off + i] = st[i];
+  }
 }
 
 // The MFMA kernel is held to 128 registers (four waves per SIMD, 16 per
 // compute unit: the memory parallelism the stream needs); it fits without
-// spilling.  The vector-ALU kernel would spill there and is left unconstrained.
+// spilling at d <= 128.  The vector-ALU kernel would spill there and is left
+// unconstrained.
 template <int R, int D, class Engine>
 __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void score_kernel_mfma(Call c) {
@@ -363,11 +468,10 @@ hipError_t launch_d(const Call& c, dim3 grid, hipStream_t s) {
 
 hipError_t launch_score(const Call& c, hipStream_t stream) {
   if (c.blocks == 0) return hipSuccess;
-  // One workgroup per piece of c.piece positions of one layer; the host cannot
-  // see how many positions are admitted, so the grid covers full admission and
-  // the surplus workgroups exit at once.
-  const int64_t per_layer = (c.blocks + c.piece - 1) / c.piece;
-  dim3 grid((unsigned)(per_layer * c.layers));
+  // The host cannot see how many positions are admitted: the grid is sized
+  // for full admission and for every resident slot, and workgroups without a
+  // piece exit at once.
+  dim3 grid((unsigned)c.score_wgs);
   switch (c.dim) {
     case 32: return launch_d<32>(c, grid, stream);
     case 64: return launch_d<64>(c, grid, stream);

@@ -3,26 +3,28 @@
 //
 // Page "DeepSeek V4.1F Q4 on M3 Ultra with native DSpark MTP (40tps /
 // 800tps)", paragraph "Decode at depth": the top 512 are taken with a radix
-// select of bounded depth.  Here the depth is at most three digits of the
-// 32-bit key (11 + 11 + 10 bits), each resolved with one LDS histogram, so the
-// work is a fixed number of passes over the row's keys whatever the data.
-//
+// select of bounded depth.  Here every pass resolves 11 more bits of a 64-bit
+// word with one LDS histogram, and the depth is bounded by the word's length
+// (six passes; one or two in practice).
+
 // A candidate is the 64-bit word (key << 32) | ~position: a larger word is a
 // higher score, or an equal score at a lower position.  Positions ascend with
 // block index, so one unsigned compare is the whole output order, ties to the
 // lower block index included.
 //
-// One workgroup per (layer, row):
-//  1. From the first-digit histogram the score kernel built, find the
-//     boundary bin B1: the highest bin whose keys, with every key above it,
-//     number at least m = min(k, admitted).
-//  2. If the keys in bins >= B1 fit the LDS buffer (the usual case: a few
-//     hundred keys sit in B1), gather them with 16-byte loads, sort them
-//     descending with an LDS bitonic network, and keep the first m.
-//  3. Otherwise (a huge run of near-equal scores), resolve digits 2 and 3 with
-//     two more histogram passes to the exact k-th key T, gather every key
-//     above T, add the ties at T in position order until m are taken (an
-//     ordered fill with a workgroup prefix sum), and sort those m.
+// One workgroup per (layer, row), m = min(k, admitted):
+//  * Usual path: the score kernel left c candidates, every key at or above the
+//    row's floor.  If c >= m the best m of the row are among them (at least m
+//    keys reach the floor, so the m-th best does, and so do all its ties).  A
+//    radix select over the candidate words (in registers when c <= 8192, else
+//    re-read from memory on each pass) narrows them to at most max(m, 1024),
+//    which are sorted descending and the first m kept.
+//  * Exact fallback (c < m: the floor was set too high): the row is rescored
+//    in fp32 over every admitted position, its words replace the candidate
+//    list, and the same select runs over all of them.
+// The sort keeps 64 or more words per wave in registers: exchanges within a
+// wave go through cross-lane shuffles, and only distances that cross waves go
+// through LDS behind a workgroup barrier.
 // Output: block indices and fp32 scores (recovered exactly from the keys),
 // then padding (-1, -inf) up to k, and the count m.
 #include "device_util.h"
@@ -32,6 +34,7 @@ namespace dssel {
 namespace {
 
 constexpr int NT = kSelectThreads;
+constexpr int kWaves = NT / kWave;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint64_t pack(uint32_t key, int pos) {
@@ -62,158 +65,238 @@ __device__ void find_boundary(const uint32_t* hist, int nbins, int need, int* ou
   __syncthreads();
 }
 
-// Order this wave's earlier LDS writes before its later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Sort se[0, n) (n a power of two) descending in LDS.  Thread t handles the
-// compare-exchange pairs t, t + NT, ...; for strides <= 64 the pairs of wave w
-// stay inside its own 128-element spans, so only stages whose neighbours cross
-// waves need a workgroup barrier.
-__device__ void bitonic_sort_desc(uint64_t* se, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = threadIdx.x; t < (n >> 1); t += NT) {
-        const int i = 2 * t - (t & (stride - 1));
-        const int j = i + stride;
-        const bool desc = (i & size) == 0;
-        const uint64_t ei = se[i], ej = se[j];
-        if (desc ? ei < ej : ei > ej) {
-          se[i] = ej;
-          se[j] = ei;
+// Sort se[0, n) descending; n is a power of two, 64 <= n <= 64 * EPL * 16.
+// Wave w holds elements [w * 64 * EPL, (w + 1) * 64 * EPL) in registers.
+template <int EPL>
+__device__ void block_sort_desc(uint64_t* se, int n) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int span = 64 * EPL;
+  const bool active = wave * span < n;
+  const int base = wave * span;
+  uint64_t v[EPL];
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = se[base + i * 64 + lane];
+  }
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= span) {  // partner in another wave: exchange through LDS
+        __syncthreads();
+        if (active) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) se[base + i * 64 + lane] = v[i];
         }
+        __syncthreads();
+        if (active) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            const int e = base + i * 64 + lane;
+            v[i] = bitonic_keep(v[i], se[e ^ j], e, k, j);
+          }
+        }
+      } else if (active) {
+        uint64_t nv[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          uint64_t p;
+          if (j < 64) {
+            p = shfl_xor_u64(v[i], j);
+          } else {  // partner register i ^ (j / 64) of the same lane
+            const int t = j >> 6;
+            p = v[i];
+#pragma unroll
+            for (int q = 1; q < EPL; q <<= 1)
+              if (t == q) p = v[i ^ q];
+          }
+          nv[i] = bitonic_keep(v[i], p, base + i * 64 + lane, k, j);
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) v[i] = nv[i];
       }
-      const int next = stride > 1 ? (stride >> 1) : size;
-      if (stride > 64 || next > 64) __syncthreads();
-      else wave_lds_sync();
     }
+  }
+  __syncthreads();
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) se[base + i * 64 + lane] = v[i];
   }
   __syncthreads();
 }
 
-// Zero-fill se[count, n) for the smallest power of two n >= count.
-__device__ int pad_pow2(uint64_t* se, int count) {
-  int n = 1;
+// Pad se[count, n) with zero words for the smallest power of two n >= max(count, 64), sort.
+__device__ void sort_prefix(uint64_t* se, int count) {
+  int n = 64;
   while (n < count) n <<= 1;
   for (int i = count + threadIdx.x; i < n; i += NT) se[i] = 0ull;
   __syncthreads();
-  return n;
+  if (n <= 1024) block_sort_desc<1>(se, n);
+  else if (n <= 2048) block_sort_desc<2>(se, n);
+  else if (n <= 4096) block_sort_desc<4>(se, n);
+  else block_sort_desc<8>(se, n);
+}
+
+struct SelectShared {
+  uint32_t hist[kHistBins];
+  uint64_t se[kSelectBuf];
+  float q[256];
+  int scan[kWaves + 1];
+  int bin, above, count;
+};
+
+// Candidate words held in registers, at most kPer per thread (c <= kSelectBuf).
+struct RegisterWords {
+  static constexpr int kPer = kSelectBuf / NT;
+  uint64_t v[kPer];
+  int c;
+  __device__ RegisterWords(const uint64_t* src, int count) : c(count) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * NT + (int)threadIdx.x;
+      v[u] = i < c ? src[i] : 0ull;
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) f(u * NT + (int)threadIdx.x < c, v[u]);
+  }
+};
+
+// Candidate words read from global memory on every pass (any count).
+struct GlobalWords {
+  const uint64_t* p;
+  int c;
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+    for (int i0 = 0; i0 < c; i0 += NT) {  // same trip count in every lane
+      const int i = i0 + (int)threadIdx.x;
+      const bool valid = i < c;
+      f(valid, valid ? p[i] : 0ull);
+    }
+  }
+};
+
+// Best m of c distinct candidate words, sorted descending into se[0, m).
+// Radix select over the 64-bit word, 11 bits per pass from the top: each pass
+// histograms the words that share the prefix fixed so far, and the boundary
+// bin extends the prefix; the words above the prefix are all selected.  Once
+// the selected words plus those sharing the prefix number at most
+// max(m, 1024) they are gathered and sorted.  The words are distinct (one per
+// position), so six passes always suffice; on the usual candidate lists one
+// or two are needed.
+template <class Words>
+__device__ void radix_select_words(const Words& src, int c, int m, SelectShared& sh) {
+  const int tid = threadIdx.x;
+  const int gather_max = m > kGatherMin ? m : kGatherMin;
+  int pbits = 0;
+  uint64_t prefix = 0;
+  int above = 0, in_range = c, need = m;
+  while (pbits < 64 && above + in_range > gather_max) {
+    const int width = 64 - pbits < kDigit1Bits ? 64 - pbits : kDigit1Bits;
+    const int shift = 64 - pbits - width;
+    for (int i = tid; i < kHistBins; i += NT) sh.hist[i] = 0u;
+    __syncthreads();
+    src.each([&](bool valid, uint64_t w) {
+      if (valid && (pbits == 0 || (w >> (64 - pbits)) == prefix))
+        atomicAdd(&sh.hist[(uint32_t)(w >> shift) & ((1u << width) - 1u)], 1u);
+    });
+    __syncthreads();
+    find_boundary(sh.hist, kHistBins, need, &sh.bin, &sh.above, sh.scan);
+    const int bin = sh.bin;
+    above += sh.above;
+    need -= sh.above;
+    in_range = (int)sh.hist[bin];
+    prefix = (prefix << width) | (uint64_t)bin;
+    pbits += width;
+    __syncthreads();  // hist, bin and above are read before the next pass resets them
+  }
+  if (tid == 0) sh.count = 0;
+  __syncthreads();
+  const uint64_t lower = pbits == 0 ? 0ull : prefix << (64 - pbits);
+  src.each([&](bool valid, uint64_t w) {
+    const bool want = valid && w >= lower;
+    const int slot = wave_append(want, &sh.count);
+    if (want && slot < kSelectBuf) sh.se[slot] = w;
+  });
+  __syncthreads();
+  const int gathered = above + in_range;
+  sort_prefix(sh.se, gathered < kSelectBuf ? gathered : kSelectBuf);
+}
+
+// Exact fallback: the floor let fewer than m keys through, so row (l, r) is
+// rescored in fp32 over every admitted position and its words replace the
+// candidate list.
+__device__ int rescore_row(const Call& c, int l, int r, uint64_t* words, SelectShared& sh) {
+  const int tid = threadIdx.x;
+  const int R = c.rows, D = c.dim;
+  const int64_t N = c.blocks, lr = (int64_t)l * R + r;
+  const int P = c.mode == kRowMask ? c.counts[(int64_t)l * kCountStride + kMaxRows]
+                                   : c.counts[(int64_t)l * kCountStride + r];
+  const int32_t* list = c.list + (int64_t)l * N;
+  const uint16_t* K = c.keys + (int64_t)l * c.key_layer_stride;
+  int64_t lim = c.limit ? (int64_t)c.limit[lr] : N;
+  lim = lim < 0 ? 0 : (lim > N ? N : lim);
+  const uint32_t* mrow =
+      c.mode == kRowMask ? c.mask + (int64_t)l * c.mask_layer_stride + r * c.mask_row_stride : nullptr;
+
+  for (int i = tid; i < D; i += NT) sh.q[i] = c.qt[lr * D + i];
+  if (tid == 0) sh.count = 0;
+  __syncthreads();
+  for (int p0 = 0; p0 < P; p0 += NT) {
+    const int p = p0 + tid;
+    bool adm = p < P;
+    int b = 0;
+    if (adm) {
+      b = c.mode == kNoMask ? p : list[p];
+      if (mrow) adm = ((mrow[b >> 5] >> (b & 31)) & 1u) && (int64_t)b < lim;
+    }
+    uint64_t w = 0;
+    if (adm) {
+      const uint16_t* krow = K + (int64_t)b * c.ldk;
+      float dot = 0.0f;
+      for (int i = 0; i < D; i += 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(krow + i);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dot = fmaf(sh.q[i + 2 * e], bf16_lo(w4[e]), dot);
+          dot = fmaf(sh.q[i + 2 * e + 1], bf16_hi(w4[e]), dot);
+        }
+      }
+      w = pack(score_to_key(dot), p);
+    }
+    const int slot = wave_append(adm, &sh.count);
+    if (adm) words[slot] = w;
+  }
+  __syncthreads();  // the words are read back by other threads of the workgroup
+  return sh.count;
 }
 
 __global__ __launch_bounds__(NT) void select_kernel(Call c) {
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint64_t se[kSelectBuf];
-  __shared__ int scan_scratch[NT / kWave + 1];
-  __shared__ int sh_bin, sh_above, sh_count;
-
+  __shared__ SelectShared sh;
   const int l = blockIdx.y, r = blockIdx.x;
   const int R = c.rows, k = c.k;
   const int64_t lr = (int64_t)l * R + r;
   const int64_t N = c.blocks;
-  const int32_t* counts = c.counts + (int64_t)l * kCountStride;
-  const int n_adm = N ? counts[r] : 0;
+  const int n_adm = N ? c.counts[(int64_t)l * kCountStride + r] : 0;
   const int m = n_adm < k ? n_adm : k;
-  const int P = (c.mode == kRowMask) ? (N ? counts[kMaxRows] : 0) : n_adm;
-  const uint32_t* keys = c.skeys + lr * c.key_row;  // 16-byte aligned rows
-  const int32_t* list = c.list + (int64_t)l * N;
+  const int P = c.mode == kRowMask ? (N ? c.counts[(int64_t)l * kCountStride + kMaxRows] : 0) : n_adm;
   int32_t* oi = c.out_idx + lr * k;
   float* os = c.out_score + lr * k;
   const int tid = threadIdx.x;
 
   if (m > 0) {
-    for (int i = tid; i < kHistBins; i += NT) hist[i] = c.hist[lr * kHistBins + i];
-    if (tid == 0) {
-      sh_count = 0;
-      sh_bin = 0;
-      sh_above = 0;
-    }
-    __syncthreads();
-    find_boundary(hist, kHistBins, m, &sh_bin, &sh_above, scan_scratch);
-    const uint32_t B1 = (uint32_t)sh_bin;
-    const int above1 = sh_above;
-    const int gathered = above1 + (int)hist[B1];
-    int n = 0;
-
-    if (gathered <= kSelectBuf) {
-      // 2. gather every key whose first digit is >= B1, four keys per load
-      constexpr int kBatch = 4;
-      const u32x4_t* k4 = reinterpret_cast<const u32x4_t*>(keys);
-      const int chunks = (P + 3) >> 2;
-      for (int c0 = 0; c0 < chunks; c0 += NT * kBatch) {
-        u32x4_t v[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int ci = c0 + u * NT + tid;
-          v[u] = ci < chunks ? k4[ci] : u32x4_t{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int p = 4 * (c0 + u * NT + tid) + e;
-            const uint32_t key = v[u][e];
-            const bool want = p < P && key != 0u && (key >> kDigit1Shift) >= B1;
-            const int slot = wave_append(want, &sh_count);
-            if (want && slot < kSelectBuf) se[slot] = pack(key, p);
-          }
-        }
-      }
-      __syncthreads();
-      n = pad_pow2(se, gathered);
-    } else {
-      // 3. bounded fallback: two more digits, then an ordered fill of the ties
-      int need = m - above1;
-      for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
-      __syncthreads();
-      for (int p = tid; p < P; p += NT) {
-        const uint32_t key = keys[p];
-        if (key != 0u && (key >> kDigit1Shift) == B1)
-          atomicAdd(&hist[(key >> kDigit2Shift) & (kHistBins - 1)], 1u);
-      }
-      __syncthreads();
-      find_boundary(hist, kHistBins, need, &sh_bin, &sh_above, scan_scratch);
-      const uint32_t prefix2 = (B1 << 11) | (uint32_t)sh_bin;
-      need -= sh_above;
-      for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
-      __syncthreads();
-      for (int p = tid; p < P; p += NT) {
-        const uint32_t key = keys[p];
-        if (key != 0u && (key >> kDigit2Shift) == prefix2)
-          atomicAdd(&hist[key & (kDigit3Bins - 1)], 1u);
-      }
-      __syncthreads();
-      find_boundary(hist, kDigit3Bins, need, &sh_bin, &sh_above, scan_scratch);
-      const uint32_t T = (prefix2 << 10) | (uint32_t)sh_bin;
-      need -= sh_above;             // ties at T still to take, >= 1
-      const int strict = m - need;  // keys > T, all of them selected
-      for (int p0 = 0; p0 < P; p0 += NT) {
-        const int p = p0 + tid;
-        const uint32_t key = p < P ? keys[p] : 0u;
-        const bool want = key > T;
-        const int slot = wave_append(want, &sh_count);
-        if (want && slot < kSelectBuf) se[slot] = pack(key, p);
-      }
-      int taken = 0;
-      for (int p0 = 0; p0 < P && taken < need; p0 += NT) {
-        const int p = p0 + tid;
-        const bool tie = p < P && keys[p] == T;
-        int chunk_total = 0;
-        const int rank = taken + block_exclusive_scan<NT>(tie ? 1 : 0, &chunk_total, scan_scratch);
-        if (tie && rank < need) se[strict + rank] = pack(T, p);
-        taken += chunk_total;
-      }
-      __syncthreads();
-      n = pad_pow2(se, m);
-    }
-    bitonic_sort_desc(se, n);
+    uint64_t* words = c.cand + lr * c.cand_stride;
+    int cands = c.cand_count[lr * kCountPad];
+    if (cands < m) cands = rescore_row(c, l, r, words, sh);
+    if (cands <= kSelectBuf) radix_select_words(RegisterWords(words, cands), cands, m, sh);
+    else radix_select_words(GlobalWords{words, cands}, cands, m, sh);
   }
 
+  const int32_t* list = c.list + (int64_t)l * N;
   for (int j = tid; j < k; j += NT) {
     if (j < m) {
-      const uint64_t e = se[j];
+      const uint64_t e = sh.se[j];
       int p = pos_of(e);
       p = p < 0 ? 0 : (p >= P ? P - 1 : p);  // in range by construction; never index past it
       oi[j] = (c.mode == kNoMask) ? p : list[p];

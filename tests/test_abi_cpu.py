@@ -135,6 +135,7 @@ def test_valid_arguments_pass(lib):
     ("dim", 96, sel.DS_SEL_E_UNSUPPORTED),
     ("dim", 100, sel.DS_SEL_E_INVALID),
     ("q", None, sel.DS_SEL_E_INVALID),
+    ("q", 0x1002, sel.DS_SEL_E_INVALID),            # not 16-byte aligned
     ("out_idx", None, sel.DS_SEL_E_INVALID),
     ("keys", None, sel.DS_SEL_E_INVALID),
     ("keys", 0x20008, sel.DS_SEL_E_INVALID),       # not 16-byte aligned
@@ -175,8 +176,11 @@ def test_bad_limits_rejected(lib):
 def test_scratch_bytes(lib):
     lim = sel.make_limits(**LIM)
     nbytes = lib.ds_sel_scratch_bytes(ctypes.byref(lim))
-    keys = 43 * 6 * 75000 * 4
-    assert keys < nbytes < keys * 1.5
+    up = lambda v: (v + 255) // 256 * 256
+    L, R, D, N = 43, 6, 128, 75000
+    expect = (up(L * R * D * 4) + up(3 * L * R * D * 2) + up(L * N * 4) + up(9 * L * 4)
+              + up(L * R * 4) + up(L * R * 32 * 4) + up(L * R * ((N + 3) // 4 * 4) * 8))
+    assert nbytes == expect
 
 
 def test_no_device_or_create(lib):

@@ -118,6 +118,43 @@ def test_fallback_with_distinct_keys(selector):
     gs.assert_bit_exact(gs.run_gpu(selector, p), gs.run_oracle(p), "fallback_distinct")
 
 
+def _column0_problem(name, col0, N, k=512, R=2):
+    """q~ = e_0 for every row (one head, weight 1), so row scores are K[b][0]: exact."""
+    L, H, d = 1, 1, 64
+    q = np.zeros((L, R, H, d), np.float32)
+    q[:, :, 0, 0] = 1.0
+    w = np.ones((L, R, H), np.float32)
+    keys = np.zeros((L, N, d), np.float32)
+    keys[0, :, 0] = col0
+    return wl.Problem(name, k, wl.f32_to_bf16_bits(q), wl.f32_to_bf16_bits(w),
+                      wl.f32_to_bf16_bits(keys), None, None, True)
+
+
+def test_many_candidates_with_ties(selector):
+    """Four distinct scores over 40000 blocks: a quarter of the row ties at the top, so
+    more candidates pass the floor than the select holds in registers (the select then
+    re-reads them from memory on every radix pass) and the tie-break decides the output."""
+    rng = np.random.default_rng(8)
+    N = 40000
+    p = _column0_problem("many_candidates", 1.0 + rng.integers(0, 4, N) / 4.0, N)
+    _print_case("many_candidates", p)
+    gs.assert_bit_exact(gs.run_gpu(selector, p), gs.run_oracle(p), "many_candidates")
+
+
+def test_rescore_when_floor_too_high(selector):
+    """The floor is placed from 512 evenly spaced blocks, (2j+1) N / 1024.  Giving exactly
+    those blocks the top scores makes the floor pass only a few dozen candidates, fewer
+    than k, so the select must rescore the whole row; the result is still exact."""
+    rng = np.random.default_rng(9)
+    N = 20000
+    col0 = 1.0 + rng.integers(0, 128, N) / 128.0          # [1, 2): below every sampled block
+    sampled = (2 * np.arange(512) + 1) * N // 1024
+    col0[sampled] = 2.0 + rng.integers(0, 128, 512) / 64.0  # [2, 4)
+    p = _column0_problem("rescore", col0, N)
+    _print_case("rescore", p)
+    gs.assert_bit_exact(gs.run_gpu(selector, p), gs.run_oracle(p), "rescore")
+
+
 @pytest.mark.parametrize("values,mask_p,shared", [("normal", None, True), ("normal", 0.4, True),
                                                   ("normal", 0.5, False)])
 def test_general_custom(selector, values, mask_p, shared):
