@@ -96,60 +96,30 @@ __device__ __forceinline__ int wave_append(bool want, int* counter) {
   return want ? base + __popcll(below) : -1;
 }
 
+// Sum of v over aligned groups of `width` lanes (4, 8, 16 or 32), left in
+// every lane of the group.  Within a row of 16 lanes the exchanges are DPP
+// moves on the vector ALU (swap neighbours, swap pairs, mirror the half row,
+// mirror the row); only the step across rows goes through the LDS crossbar.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float group_sum(float v, int width) {
+  v += dpp_f32<0xB1>(v);                 // quad_perm [1, 0, 3, 2]: lane ^ 1
+  v += dpp_f32<0x4E>(v);                 // quad_perm [2, 3, 0, 1]: lane ^ 2
+  if (width >= 8) v += dpp_f32<0x141>(v);   // row_half_mirror: the other quad of 8
+  if (width >= 16) v += dpp_f32<0x140>(v);  // row_mirror: the other half of 16
+  if (width >= 32) v += __shfl_xor(v, 16, kWave);
+  return v;
+}
+
 // Order this wave's earlier LDS writes before its later LDS reads (the lanes
 // of one wave execute together; this only stops the compiler reordering).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, mask, kWave);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), mask, kWave);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
-  return (uint32_t)__shfl_xor((int)v, mask, kWave);
-}
-
-// One compare-exchange step of a descending bitonic network on element e
-// (value v, partner value p): block size k, distance j.
-template <typename T>
-__device__ __forceinline__ T bitonic_keep(T v, T p, int e, int k, int j) {
-  const bool desc = (e & k) == 0;
-  const bool low = (e & j) == 0;
-  const bool take_max = desc == low;
-  return take_max ? (v > p ? v : p) : (v < p ? v : p);
-}
-
-// Sort the 64 * EPL values held by one wave in descending order, in registers.
-// Element e = i * 64 + lane lives in v[i] of that lane; distances below 64
-// exchange across lanes, larger ones between the lane's own registers.
-template <int EPL, typename T>
-__device__ __forceinline__ void wave_sort_desc(T (&v)[EPL]) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int k = 2; k <= 64 * EPL; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      T nv[EPL];
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        T p;
-        if (j < 64) {
-          if constexpr (sizeof(T) == 8) p = shfl_xor_u64(v[i], j);
-          else p = shfl_xor_u32(v[i], j);
-        } else {
-          p = v[i ^ (j >> 6)];
-        }
-        nv[i] = bitonic_keep(v[i], p, i * 64 + lane, k, j);
-      }
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) v[i] = nv[i];
-    }
-  }
 }
 
 }  // namespace dssel

@@ -37,7 +37,7 @@ constexpr int kCountPad = 32;                // candidate counters sit 128 bytes
 
 constexpr int kSelectThreads = 1024;         // 16 waves
 constexpr int kSelectBuf = 8192;             // LDS candidate slots; also the most held in registers
-constexpr int kGatherMin = 1024;             // radix passes stop once this many words remain
+constexpr int kGatherSlack = 64;             // radix passes stop once m + this many words remain
 
 enum AdmitMode : int {
   kNoMask = 0,      // admitted = b < limit: the compacted index is the identity

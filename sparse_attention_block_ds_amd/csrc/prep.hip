@@ -25,14 +25,15 @@
 //
 // Candidate floors (workgroup 0): the key stream writes only keys that can
 // still be among a row's best k, i.e. keys at or above the row's floor.  The
-// floor comes from 512 blocks spread evenly over the layer: their keys are
-// sorted per row, and the floor is the sample key about three times more
-// selective than k would suggest (rank 3 k n_sample / n_admitted, plus 8).
-// Any floor is safe: the candidate lists have room for every position, and
-// the select rescores the row exactly when fewer than min(k, admitted)
-// candidates came through.  The floor only decides how few keys are written;
-// at 512 samples and 75000 admitted blocks the expected sample count above the
-// k-th key is 3.5 and the rank taken is 19, so a rescore is a ~1e-8 event.
+// floor comes from 512 blocks spread evenly over [0, N), scored on the
+// matrix cores: per row, the floor is the sampled key of rank about three
+// times more selective than k would suggest (3 k n_sample / n_admitted, plus
+// 8), found by a bitwise search over the wave's ballots.  Any floor is safe:
+// the candidate lists have room for every position, and the select rescores
+// the row exactly when fewer than min(k, admitted) candidates came through.
+// The floor only decides how few keys are written; at 512 samples and 75000
+// admitted blocks the expected sample count above the k-th key is 3.5 and the
+// rank taken is 19, so a rescore is a ~1e-8 event.
 #include "device_util.h"
 #include "dssel_internal.h"
 
@@ -108,78 +109,92 @@ union PrepShared {
   ExpandShared e;
 };
 
-// Block of sample slot j: (2 j + 1) * maxlim / (2 S) with S = min(512, maxlim),
-// i.e. the middle of the j-th of S equal stretches of [0, maxlim).
-__device__ __forceinline__ int64_t sample_block(int j, int64_t maxlim) {
-  return maxlim >= kSampleSlots ? ((2 * (int64_t)j + 1) * maxlim) >> 10 : j;
+// Block of sample slot j: (2 j + 1) * N / (2 S) with S = min(512, N), i.e. the
+// middle of the j-th of S equal stretches of [0, N).
+__device__ __forceinline__ int64_t sample_block(int j, int64_t n) {
+  return n >= kSampleSlots ? ((2 * (int64_t)j + 1) * n) >> 10 : j;
 }
 static_assert(kSampleSlots == 512, "sample_block divides by 2 * 512 with a shift");
 
-// The sample slots one thread serves: d/8 lanes share a sampled block, each
-// holding 16 bytes of its key row and, for the rows it writes (r % (d/8) ==
-// its slice), the mask word of the block.
-template <int R, int NP>
-struct SampleLoads {
-  static constexpr int kRowsPerLane = 2;  // d = 32: 4 lanes per block, up to 8 rows
-  uint4 k[NP];
-  uint32_t mw[NP][kRowsPerLane];
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-  __device__ void issue(const Call& c, int l, int64_t maxlim, const uint32_t* mask_l, int p0,
-                        int passes, int S) {
-    const int LPR = c.dim / 8, per_pass = kPrepThreads / LPR;
-    const int slice = threadIdx.x % LPR, sub = threadIdx.x / LPR;
+constexpr int kSampleGroups = kSampleSlots / 16;                // 16 sampled blocks per MFMA
+constexpr int kGroupsPerWave = kSampleGroups / (kPrepThreads / kWave);  // 2
+
+// Sampled keys on the matrix cores.  A floor only has to be a reasonable
+// guess (any floor is exact, see above), so the sampled scores use q~
+// rounded to bf16: one v_mfma_f32_16x16x32_bf16 per 32 columns gives 16
+// sampled blocks (B columns, block = lane % 16) against query rows 0-7 (A rows,
+// row = lane % 16, rows >= R zero).  Lane l then holds rows 4 (l / 16) + i of
+// block l % 16.  Each wave takes groups wave and wave + 16 of 16 slots.
+template <int R, int D>
+struct SampleMfma {
+  static constexpr int KC = D / 32;
+  u32x4_t kb[kGroupsPerWave][KC];
+  uint32_t mw[kGroupsPerWave][4];  // mask words of rows 4 (lane / 16) + i at the lane's block
+
+  __device__ void issue(const Call& c, int l, int64_t n, const uint32_t* mask_l, int S) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
     const uint16_t* K = c.keys + (int64_t)l * c.key_layer_stride;
 #pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int j = (p0 + u) * per_pass + sub;
-      k[u] = uint4{0u, 0u, 0u, 0u};
+    for (int g = 0; g < kGroupsPerWave; ++g) {
+      const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
 #pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i) mw[u][i] = 0xFFFFFFFFu;
-      if (p0 + u < passes && j < S) {
-        const int64_t b = sample_block(j, maxlim);
-        k[u] = *reinterpret_cast<const uint4*>(K + b * c.ldk + slice * 8);
+      for (int cc = 0; cc < KC; ++cc) kb[g][cc] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mw[g][i] = 0xFFFFFFFFu;
+      if (j < S) {
+        const int64_t b = sample_block(j, n);
+        const uint16_t* row = K + b * c.ldk + 8 * (lane >> 4);
+#pragma unroll
+        for (int cc = 0; cc < KC; ++cc) kb[g][cc] = *reinterpret_cast<const u32x4_t*>(row + 32 * cc);
         if (c.mode == kSharedMask) {
-          mw[u][0] = mw[u][1] = mask_l[b >> 5];
+          const uint32_t w = mask_l[b >> 5];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mw[g][i] = w;
         } else if (c.mode == kRowMask) {
 #pragma unroll
-          for (int i = 0; i < kRowsPerLane; ++i) {
-            const int r = slice + i * LPR;
-            if (r < R) mw[u][i] = mask_l[r * c.mask_row_stride + (b >> 5)];
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * (lane >> 4) + i;
+            if (r < R) mw[g][i] = mask_l[r * c.mask_row_stride + (b >> 5)];
           }
         }
       }
     }
   }
 
-  // Dot the held rows with q~ and store the admitted rows' keys.
-  __device__ void finish(const Call& c, int64_t maxlim, int p0, int passes, int S,
-                         const float (&qv)[R][8], FoldShared& sh) {
-    const int LPR = c.dim / 8, per_pass = kPrepThreads / LPR;
-    const int slice = threadIdx.x % LPR, sub = threadIdx.x / LPR;
+  __device__ void finish(int64_t n, int S, FoldShared& sh) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int m = lane & 15;
+    bf16x8_t a[KC];
 #pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int j = (p0 + u) * per_pass + sub;
-      const uint32_t k4[4] = {k[u].x, k[u].y, k[u].z, k[u].w};
-      float d[R];
+    for (int cc = 0; cc < KC; ++cc) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (m < R) {
+        const float* qr = &sh.q[m < R ? m : 0][32 * cc + 8 * (lane >> 4)];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        d[r] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d[r] = fmaf(qv[r][2 * e], bf16_lo(k4[e]), d[r]);
-          d[r] = fmaf(qv[r][2 * e + 1], bf16_hi(k4[e]), d[r]);
-        }
+        for (int e = 0; e < 4; ++e)
+          v[e] = (uint32_t)f32_to_bf16_rne(qr[2 * e]) | ((uint32_t)f32_to_bf16_rne(qr[2 * e + 1]) << 16);
       }
-      for (int m = 1; m < LPR; m <<= 1)
+      a[cc] = __builtin_bit_cast(bf16x8_t, v);
+    }
 #pragma unroll
-        for (int r = 0; r < R; ++r) d[r] += __shfl_xor(d[r], m, kWave);
-      if (p0 + u < passes && j < S) {
-        const int64_t b = sample_block(j, maxlim);
+    for (int g = 0; g < kGroupsPerWave; ++g) {
+      const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (r % LPR != slice) continue;
-          const uint32_t w = r < LPR ? mw[u][0] : mw[u][1];
-          if (b < sh.lim[r] && ((w >> (b & 31)) & 1u)) sh.skey[r][j] = score_to_key(d[r]);
+      for (int cc = 0; cc < KC; ++cc)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[cc], __builtin_bit_cast(bf16x8_t, kb[g][cc]), acc,
+                                                      0, 0, 0);
+      if (j < S) {
+        const int64_t b = sample_block(j, n);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * (lane >> 4) + i;
+          if (r < R && b < sh.lim[r] && ((mw[g][i] >> (b & 31)) & 1u))
+            sh.skey[r][j] = score_to_key(acc[i]);
         }
       }
     }
@@ -190,6 +205,7 @@ struct SampleLoads {
 // with at least j keys >= x, built bit by bit from the top.
 __device__ __forceinline__ uint32_t wave_jth_largest(const uint32_t (&v)[kSampleSlots / kWave], int j) {
   uint32_t x = 0;
+#pragma unroll 1
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t t = x | (1u << bit);
     int n = 0;
@@ -203,10 +219,9 @@ __device__ __forceinline__ uint32_t wave_jth_largest(const uint32_t (&v)[kSample
 // Workgroup 0 of layer l: counts, fold, floors.  Every global load the
 // workgroup needs (sampled key rows and their mask words, the query heads and
 // weights, the mask words to count) is issued before any of them is used.
-template <int R>
+template <int R, int D>
 __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
-  constexpr int NP = R <= 6 ? 8 : 4;  // sample passes in flight
-  const int D = c.dim, H = c.heads;
+  const int H = c.heads;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const Limits s = layer_limits(c, l);
   const uint32_t* mask_l = c.mask ? c.mask + (int64_t)l * c.mask_layer_stride : nullptr;
@@ -216,11 +231,22 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
   if (tid < kMaxRows) sh.lim[tid] = tid < R ? clamp_limit(c.limit, (int64_t)l * R + tid, c.blocks) : 0;
   for (int i = tid; i < kMaxRows * kSampleSlots; i += kPrepThreads) (&sh.skey[0][0])[i] = 0u;
 
-  // sampled key rows (the first NP passes)
-  const int S = s.maxlim < kSampleSlots ? (int)s.maxlim : kSampleSlots;
-  const int passes = (S * (D / 8) + kPrepThreads - 1) / kPrepThreads;
-  SampleLoads<R, NP> smp;
-  smp.issue(c, l, s.maxlim, mask_l, 0, passes, S);
+  // sampled key rows: spread over [0, N), so that their addresses wait for
+  // nothing; samples at or past a row's limit are simply not admitted
+  const int64_t N = c.blocks;
+  const int S = N < kSampleSlots ? (int)N : kSampleSlots;
+  SampleMfma<R, D> smp;
+  smp.issue(c, l, N, mask_l, S);
+
+  // the mask words to count, when every row shares one mask row
+  constexpr int kCountWords = 4;  // per thread in flight: masks up to 131072 blocks
+  const int64_t words = (s.maxlim + 31) / 32;
+  uint32_t cw[kCountWords];
+#pragma unroll
+  for (int i = 0; i < kCountWords; ++i) {
+    const int64_t j = tid + (int64_t)i * kPrepThreads;
+    cw[i] = (c.mode == kSharedMask && j < words) ? mask_l[j] : 0u;
+  }
 
   // fold, first half: thread (slice hs, chunk) sums w_h q_h[i0 .. i0 + 8) over
   // its slice of heads, ascending h, eight heads' loads at a time
@@ -265,11 +291,23 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
     if (tid < R) sh.acc[tid] = (int)sh.lim[tid];
     if (tid == 0) sh.acc[kMaxRows] = (int)s.maxlim;
   } else {
-    const int64_t words = (s.maxlim + 31) / 32;
     int rc[kMaxRows + 1];
 #pragma unroll
     for (int r = 0; r <= kMaxRows; ++r) rc[r] = 0;
-    for (int64_t j = tid; j < words; j += kPrepThreads) {
+    int64_t j0 = tid;
+    if (c.mode == kSharedMask) {
+#pragma unroll
+      for (int i = 0; i < kCountWords; ++i) {
+        const int64_t j = tid + (int64_t)i * kPrepThreads;
+        if (j < words) {
+          rc[kMaxRows] += __popc(cw[i] & below_limit_bits(j, s.maxlim));
+#pragma unroll
+          for (int r = 0; r < R; ++r) rc[r] += __popc(cw[i] & below_limit_bits(j, s.lim[r]));
+        }
+      }
+      j0 = tid + (int64_t)kCountWords * kPrepThreads;
+    }
+    for (int64_t j = j0; j < words; j += kPrepThreads) {
       rc[kMaxRows] += __popc(union_word(c, mask_l, s, j));
 #pragma unroll
       for (int r = 0; r < R; ++r) rc[r] += __popc(row_word(c, mask_l, s, r, j));
@@ -306,19 +344,7 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
   if (tid <= kMaxRows && (tid < R || tid == kMaxRows)) counts[tid] = sh.acc[tid];
 
   // sample keys
-  {
-    const int slice = tid % (D / 8);
-    float qv[R][8];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[r][e] = sh.q[r][slice * 8 + e];
-    smp.finish(c, s.maxlim, 0, passes, S, qv, sh);
-    for (int p0 = NP; p0 < passes; p0 += NP) {  // d = 256: the rest of the passes
-      smp.issue(c, l, s.maxlim, mask_l, p0, passes, S);
-      smp.finish(c, s.maxlim, p0, passes, S, qv, sh);
-    }
-  }
+  smp.finish(N, S, sh);
   __syncthreads();
 
   // floors: wave r finds row r's jth largest sample key
@@ -389,11 +415,23 @@ __device__ void expand_tiles(const Call& c, int l, int x, ExpandShared& sh) {
   for (int i = lane; i < tile_total; i += kWave) out[i] = sh.stage[wave][i];
 }
 
-template <int R>
+template <int R, int D>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(Call c) {
   __shared__ PrepShared sh;
-  if (blockIdx.x == 0) fold_count_floor<R>(c, blockIdx.y, sh.f);
+  if (blockIdx.x == 0) fold_count_floor<R, D>(c, blockIdx.y, sh.f);
   else expand_tiles(c, blockIdx.y, blockIdx.x, sh.e);
+}
+
+template <int R>
+hipError_t launch_r(const Call& c, dim3 grid, hipStream_t stream) {
+  switch (c.dim) {
+    case 32: hipLaunchKernelGGL((prep_kernel<R, 32>), grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 64: hipLaunchKernelGGL((prep_kernel<R, 64>), grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 128: hipLaunchKernelGGL((prep_kernel<R, 128>), grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 256: hipLaunchKernelGGL((prep_kernel<R, 256>), grid, dim3(kPrepThreads), 0, stream, c); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -402,17 +440,16 @@ hipError_t launch_prep(const Call& c, hipStream_t stream) {
   const int expanders = c.mode == kNoMask ? 0 : (c.ntiles + kPrepTilesPerWg - 1) / kPrepTilesPerWg;
   dim3 grid(1 + expanders, c.layers);
   switch (c.rows) {
-    case 1: hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(kPrepThreads), 0, stream, c); break;
-    case 2: hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(kPrepThreads), 0, stream, c); break;
-    case 3: hipLaunchKernelGGL(prep_kernel<3>, grid, dim3(kPrepThreads), 0, stream, c); break;
-    case 4: hipLaunchKernelGGL(prep_kernel<4>, grid, dim3(kPrepThreads), 0, stream, c); break;
-    case 5: hipLaunchKernelGGL(prep_kernel<5>, grid, dim3(kPrepThreads), 0, stream, c); break;
-    case 6: hipLaunchKernelGGL(prep_kernel<6>, grid, dim3(kPrepThreads), 0, stream, c); break;
-    case 7: hipLaunchKernelGGL(prep_kernel<7>, grid, dim3(kPrepThreads), 0, stream, c); break;
-    case 8: hipLaunchKernelGGL(prep_kernel<8>, grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 1: return launch_r<1>(c, grid, stream);
+    case 2: return launch_r<2>(c, grid, stream);
+    case 3: return launch_r<3>(c, grid, stream);
+    case 4: return launch_r<4>(c, grid, stream);
+    case 5: return launch_r<5>(c, grid, stream);
+    case 6: return launch_r<6>(c, grid, stream);
+    case 7: return launch_r<7>(c, grid, stream);
+    case 8: return launch_r<8>(c, grid, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace dssel

@@ -18,13 +18,13 @@
 //    keys reach the floor, so the m-th best does, and so do all its ties).  A
 //    radix select over the candidate words (in registers when c <= 8192, else
 //    re-read from memory on each pass) narrows them to at most max(m, 1024),
-//    which are sorted descending and the first m kept.
+//    whose best m are placed in descending order.
 //  * Exact fallback (c < m: the floor was set too high): the row is rescored
 //    in fp32 over every admitted position, its words replace the candidate
 //    list, and the same select runs over all of them.
-// The sort keeps 64 or more words per wave in registers: exchanges within a
-// wave go through cross-lane shuffles, and only distances that cross waves go
-// through LDS behind a workgroup barrier.
+// The final order: the gathered words are sorted in runs of 64 (one per wave,
+// in registers), and each word's place is the number of larger words, found
+// by a binary search in every run.
 // Output: block indices and fp32 scores (recovered exactly from the keys),
 // then padding (-1, -inf) up to k, and the count m.
 #include "device_util.h"
@@ -65,79 +65,66 @@ __device__ void find_boundary(const uint32_t* hist, int nbins, int need, int* ou
   __syncthreads();
 }
 
-// Sort se[0, n) descending; n is a power of two, 64 <= n <= 64 * EPL * 16.
-// Wave w holds elements [w * 64 * EPL, (w + 1) * 64 * EPL) in registers.
-template <int EPL>
-__device__ void block_sort_desc(uint64_t* se, int n) {
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int span = 64 * EPL;
-  const bool active = wave * span < n;
-  const int base = wave * span;
-  uint64_t v[EPL];
-  if (active) {
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) v[i] = se[base + i * 64 + lane];
-  }
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= span) {  // partner in another wave: exchange through LDS
-        __syncthreads();
-        if (active) {
-#pragma unroll
-          for (int i = 0; i < EPL; ++i) se[base + i * 64 + lane] = v[i];
-        }
-        __syncthreads();
-        if (active) {
-#pragma unroll
-          for (int i = 0; i < EPL; ++i) {
-            const int e = base + i * 64 + lane;
-            v[i] = bitonic_keep(v[i], se[e ^ j], e, k, j);
-          }
-        }
-      } else if (active) {
-        uint64_t nv[EPL];
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          uint64_t p;
-          if (j < 64) {
-            p = shfl_xor_u64(v[i], j);
-          } else {  // partner register i ^ (j / 64) of the same lane
-            const int t = j >> 6;
-            p = v[i];
-#pragma unroll
-            for (int q = 1; q < EPL; q <<= 1)
-              if (t == q) p = v[i ^ q];
-          }
-          nv[i] = bitonic_keep(v[i], p, base + i * 64 + lane, k, j);
-        }
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) v[i] = nv[i];
-      }
-    }
+constexpr int kRun = kWave;  // words per sorted run: one per lane of a wave
+
+// One compare-exchange step of a descending bitonic network on element e
+// (value v, partner value p): block size k, distance j.
+__device__ __forceinline__ uint64_t bitonic_keep(uint64_t v, uint64_t p, int e, int k, int j) {
+  const bool desc = (e & k) == 0;
+  const bool low = (e & j) == 0;
+  return (desc == low) ? (v > p ? v : p) : (v < p ? v : p);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, mask, kWave);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), mask, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The best m of the n distinct words se[0, n), in descending order, into
+// out[0, min(n, m)).  The words are cut into runs of 64; each wave sorts runs
+// in registers (a bitonic network across its lanes), and a word's place is
+// the number of larger words, summed over the runs by a binary search in
+// each.  se[n, 64 * ceil(n / 64)) must hold zero words, which are never larger
+// than a candidate.
+__device__ void sort_place(uint64_t* se, int n, int m, uint64_t* out) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int runs = (n + kRun - 1) / kRun;  // <= 2 NT / 64 = 32
+  for (int run = wave; run < runs; run += NT / kWave) {
+    uint64_t v = se[run * kRun + lane];
+    for (int k = 2; k <= kRun; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) v = bitonic_keep(v, shfl_xor_u64(v, j), lane, k, j);
+    se[run * kRun + lane] = v;
   }
   __syncthreads();
-  if (active) {
+  for (int idx = tid; idx < runs * kRun; idx += NT) {
+    const uint64_t e = se[idx];
+    if (e == 0ull) continue;  // padding
+    int place = 0;
+    for (int r0 = 0; r0 < runs; r0 += 8) {  // eight runs' searches interleaved
+      int cnt[8];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) se[base + i * 64 + lane] = v[i];
+      for (int t = 0; t < 8; ++t) cnt[t] = 0;
+#pragma unroll
+      for (int step = kRun / 2; step > 0; step >>= 1) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (r0 + t < runs && se[(r0 + t) * kRun + cnt[t] + step - 1] > e) cnt[t] += step;
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (r0 + t < runs) place += cnt[t] + (se[(r0 + t) * kRun + cnt[t]] > e ? 1 : 0);
+    }
+    if (place < m) out[place] = e;
   }
   __syncthreads();
 }
 
-// Pad se[count, n) with zero words for the smallest power of two n >= max(count, 64), sort.
-__device__ void sort_prefix(uint64_t* se, int count) {
-  int n = 64;
-  while (n < count) n <<= 1;
-  for (int i = count + threadIdx.x; i < n; i += NT) se[i] = 0ull;
-  __syncthreads();
-  if (n <= 1024) block_sort_desc<1>(se, n);
-  else if (n <= 2048) block_sort_desc<2>(se, n);
-  else if (n <= 4096) block_sort_desc<4>(se, n);
-  else block_sort_desc<8>(se, n);
-}
+constexpr int kGatherCap = kSelectBuf / 2;  // gathered words; the sorted best m follow them
 
 struct SelectShared {
   uint32_t hist[kHistBins];
-  uint64_t se[kSelectBuf];
+  uint64_t se[kSelectBuf];  // [0, kGatherCap): gathered words; [kGatherCap, ...): the best m, sorted
   float q[256];
   int scan[kWaves + 1];
   int bin, above, count;
@@ -176,18 +163,18 @@ struct GlobalWords {
   }
 };
 
-// Best m of c distinct candidate words, sorted descending into se[0, m).
-// Radix select over the 64-bit word, 11 bits per pass from the top: each pass
-// histograms the words that share the prefix fixed so far, and the boundary
-// bin extends the prefix; the words above the prefix are all selected.  Once
-// the selected words plus those sharing the prefix number at most
-// max(m, 1024) they are gathered and sorted.  The words are distinct (one per
-// position), so six passes always suffice; on the usual candidate lists one
-// or two are needed.
+// Best m of c distinct candidate words, sorted descending.  Radix select over
+// the 64-bit word, 11 bits per pass from the top: each pass histograms the
+// words that share the prefix fixed so far, and the boundary bin extends the
+// prefix; the words above the prefix are all selected.  The passes go on
+// until the selected words plus those sharing the prefix number at most
+// m + kGatherSlack; then they are gathered and ordered.  The words are distinct
+// (one per position), so six passes always suffice; on the usual candidate
+// lists one or two are needed.
 template <class Words>
 __device__ void radix_select_words(const Words& src, int c, int m, SelectShared& sh) {
   const int tid = threadIdx.x;
-  const int gather_max = m > kGatherMin ? m : kGatherMin;
+  const int gather_max = m + kGatherSlack < 2 * NT ? m + kGatherSlack : 2 * NT;  // >= m
   int pbits = 0;
   uint64_t prefix = 0;
   int above = 0, in_range = c, need = m;
@@ -216,11 +203,13 @@ __device__ void radix_select_words(const Words& src, int c, int m, SelectShared&
   src.each([&](bool valid, uint64_t w) {
     const bool want = valid && w >= lower;
     const int slot = wave_append(want, &sh.count);
-    if (want && slot < kSelectBuf) sh.se[slot] = w;
+    if (want && slot < kGatherCap) sh.se[slot] = w;
   });
+  int gathered = above + in_range;  // <= gather_max <= 2 NT
+  gathered = gathered < 2 * NT ? gathered : 2 * NT;
+  if (tid < kRun) sh.se[gathered + tid] = 0ull;
   __syncthreads();
-  const int gathered = above + in_range;
-  sort_prefix(sh.se, gathered < kSelectBuf ? gathered : kSelectBuf);
+  sort_place(sh.se, gathered, m, sh.se + kGatherCap);
 }
 
 // Exact fallback: the floor let fewer than m keys through, so row (l, r) is
@@ -296,7 +285,7 @@ __global__ __launch_bounds__(NT) void select_kernel(Call c) {
   const int32_t* list = c.list + (int64_t)l * N;
   for (int j = tid; j < k; j += NT) {
     if (j < m) {
-      const uint64_t e = sh.se[j];
+      const uint64_t e = sh.se[kGatherCap + j];
       int p = pos_of(e);
       p = p < 0 ? 0 : (p >= P ? P - 1 : p);  // in range by construction; never index past it
       oi[j] = (c.mode == kNoMask) ? p : list[p];
