@@ -3,9 +3,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sweep]
 
-A step is one call of the whole chain (admission + compaction + fold, the
-shared key stream with its radix keys and first-digit histograms, the bounded
-radix select and the ordered output) over one batch of synthetic input that is
+A step is one call of the whole chain (admission + compaction + fold +
+candidate floors, the shared key stream that scores every admitted block for
+every row and keeps the keys at or above each row's floor, the bounded radix
+select with the ordered output) over one batch of synthetic input that is
 already resident in HBM.  The default workload is the 43-layer sweep at 300k
 context (43 layers x 6 verify rows x 75,000 compressed blocks, d = 128,
 H = 64, k = 512), whose 826 MB of keys exceed the 256 MB Infinity Cache, so
@@ -131,7 +132,9 @@ def cpu_baseline(p, gpu_out, budget_s):
 
     lib = oracle.load()
     g_idx, g_score, g_count = gpu_out
-    order = [(l, r) for l in range(0, p.layers, max(1, p.layers // 4)) for r in range(p.rows)]
+    step = max(1, p.layers // 4)
+    layers = list(range(0, p.layers, step)) + [l for l in range(p.layers) if l % step]
+    order = [(l, r) for l in layers for r in range(p.rows)]
     per_row, _ = admitted_counts(p)
     done, cand, spent, mismatches = [], 0, 0.0, 0
     for l, r in order:

@@ -48,10 +48,15 @@ __device__ __forceinline__ int64_t clamp_limit(const int32_t* limit, int64_t idx
   return v < 0 ? 0 : (v > n ? n : v);
 }
 
+// Sum over the wave, uniform result: DPP sums within each row of 16 lanes,
+// then the four row sums read out to scalars.
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // lane ^ 2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // other quad of 8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // other half of 16
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
 struct Limits {
@@ -201,12 +206,15 @@ struct SampleMfma {
   }
 };
 
-// The j-th largest of the 512 keys a wave holds (8 per lane): the largest x
-// with at least j keys >= x, built bit by bit from the top.
+// A floor for the j-th largest of the 512 keys a wave holds (8 per lane): the
+// largest x with at least j keys >= x, built bit by bit from the top, over
+// the top 16 bits only (sign, exponent and 7 mantissa bits of the score).
+// It is at most the j-th largest key and lets through at most the keys that
+// share its 16-bit prefix besides.
 __device__ __forceinline__ uint32_t wave_jth_largest(const uint32_t (&v)[kSampleSlots / kWave], int j) {
   uint32_t x = 0;
 #pragma unroll 1
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = 31; bit >= 16; --bit) {
     const uint32_t t = x | (1u << bit);
     int n = 0;
 #pragma unroll
@@ -227,26 +235,24 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
   const uint32_t* mask_l = c.mask ? c.mask + (int64_t)l * c.mask_layer_stride : nullptr;
   int32_t* counts = c.counts + (int64_t)l * kCountStride;
 
-  if (tid <= kMaxRows) sh.acc[tid] = 0;
-  if (tid < kMaxRows) sh.lim[tid] = tid < R ? clamp_limit(c.limit, (int64_t)l * R + tid, c.blocks) : 0;
-  for (int i = tid; i < kMaxRows * kSampleSlots; i += kPrepThreads) (&sh.skey[0][0])[i] = 0u;
-
-  // sampled key rows: spread over [0, N), so that their addresses wait for
-  // nothing; samples at or past a row's limit are simply not admitted
+  // Sampled key rows: spread over [0, N), so that their addresses wait for
+  // nothing (samples at or past a row's limit are simply not admitted).
   const int64_t N = c.blocks;
   const int S = N < kSampleSlots ? (int)N : kSampleSlots;
   SampleMfma<R, D> smp;
   smp.issue(c, l, N, mask_l, S);
 
-  // the mask words to count, when every row shares one mask row
+  // The mask words to count, when every row shares one mask row (all words
+  // below N: the limits are applied when counting).
   constexpr int kCountWords = 4;  // per thread in flight: masks up to 131072 blocks
-  const int64_t words = (s.maxlim + 31) / 32;
+  const int64_t all_words = (N + 31) / 32;
   uint32_t cw[kCountWords];
 #pragma unroll
   for (int i = 0; i < kCountWords; ++i) {
     const int64_t j = tid + (int64_t)i * kPrepThreads;
-    cw[i] = (c.mode == kSharedMask && j < words) ? mask_l[j] : 0u;
+    cw[i] = (c.mode == kSharedMask && j < all_words) ? mask_l[j] : 0u;
   }
+  for (int i = tid; i < kMaxRows * kSampleSlots; i += kPrepThreads) (&sh.skey[0][0])[i] = 0u;
 
   // fold, first half: thread (slice hs, chunk) sums w_h q_h[i0 .. i0 + 8) over
   // its slice of heads, ascending h, eight heads' loads at a time
@@ -285,8 +291,12 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
     for (int e = 0; e < 8; ++e) sh.part[hs * R * D + r * D + i0 + e] = acc[e];
   }
 
+  if (tid <= kMaxRows) sh.acc[tid] = 0;
+  if (tid < kMaxRows) sh.lim[tid] = tid < R ? clamp_limit(c.limit, (int64_t)l * R + tid, N) : 0;
+
   // admitted counts per row and for the union
   __syncthreads();
+  const int64_t words = (s.maxlim + 31) / 32;
   if (c.mode == kNoMask) {
     if (tid < R) sh.acc[tid] = (int)sh.lim[tid];
     if (tid == 0) sh.acc[kMaxRows] = (int)s.maxlim;
