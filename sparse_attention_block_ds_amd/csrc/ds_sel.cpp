@@ -18,6 +18,9 @@ struct ds_sel {
           off_cand = 0;
 };
 
+// The select orders at most 2048 winners per row in LDS.
+static_assert(DS_SEL_MAX_K <= 2048, "select kernel LDS sized for k <= 2048");
+
 namespace {
 
 constexpr int64_t kAlign = 256;

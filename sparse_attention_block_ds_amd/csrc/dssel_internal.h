@@ -35,8 +35,7 @@ constexpr int kScoreWgsPerCu = 4;            // resident score workgroups per co
 constexpr int kWaveCandBuf = 128;            // per-wave, per-row candidate staging (LDS)
 constexpr int kCountPad = 32;                // candidate counters sit 128 bytes apart
 
-constexpr int kSelectThreads = 1024;         // 16 waves
-constexpr int kSelectBuf = 8192;             // LDS candidate slots; also the most held in registers
+constexpr int kSelectBuf = 8192;             // candidates the select holds in registers
 constexpr int kGatherSlack = 64;             // radix passes stop once m + this many words remain
 
 enum AdmitMode : int {

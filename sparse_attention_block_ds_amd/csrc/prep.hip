@@ -42,12 +42,6 @@ namespace {
 
 constexpr int kPrepWaves = kPrepThreads / kWave;
 
-__device__ __forceinline__ int64_t clamp_limit(const int32_t* limit, int64_t idx, int64_t n) {
-  if (!limit) return n;
-  const int64_t v = limit[idx];
-  return v < 0 ? 0 : (v > n ? n : v);
-}
-
 // Sum over the wave, uniform result: DPP sums within each row of 16 lanes,
 // then the four row sums read out to scalars.
 __device__ __forceinline__ int wave_sum(int v) {
@@ -64,25 +58,38 @@ struct Limits {
   int64_t maxlim;
 };
 
+// The layer's R limits, clamped to [0, N]: R independent loads, then the clamps.
+template <int R>
 __device__ __forceinline__ Limits layer_limits(const Call& c, int l) {
   Limits s;
+  int64_t raw[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) raw[r] = c.blocks;
+  if (c.limit) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) raw[r] = c.limit[(int64_t)l * R + r];
+  }
   s.maxlim = 0;
 #pragma unroll
   for (int r = 0; r < kMaxRows; ++r) {
-    s.lim[r] = r < c.rows ? clamp_limit(c.limit, (int64_t)l * c.rows + r, c.blocks) : 0;
+    const int64_t v = r < R ? raw[r < R ? r : 0] : 0;
+    s.lim[r] = v < 0 ? 0 : (v > c.blocks ? c.blocks : v);
     s.maxlim = s.lim[r] > s.maxlim ? s.lim[r] : s.maxlim;
   }
   return s;
 }
 
 // Union of the rows' admitted blocks in mask word j (blocks 32 j .. 32 j + 31).
+template <int R>
 __device__ __forceinline__ uint32_t union_word(const Call& c, const uint32_t* mask_l, const Limits& s,
                                                int64_t j) {
   if (c.mode == kSharedMask) return mask_l[j] & below_limit_bits(j, s.maxlim);
+  uint32_t w[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) w[r] = mask_l[r * c.mask_row_stride + j];
   uint32_t u = 0;
 #pragma unroll
-  for (int r = 0; r < kMaxRows; ++r)
-    if (r < c.rows) u |= mask_l[r * c.mask_row_stride + j] & below_limit_bits(j, s.lim[r]);
+  for (int r = 0; r < R; ++r) u |= w[r] & below_limit_bits(j, s.lim[r]);
   return u;
 }
 
@@ -231,7 +238,7 @@ template <int R, int D>
 __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
   const int H = c.heads;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const Limits s = layer_limits(c, l);
+  const Limits s = layer_limits<R>(c, l);
   const uint32_t* mask_l = c.mask ? c.mask + (int64_t)l * c.mask_layer_stride : nullptr;
   int32_t* counts = c.counts + (int64_t)l * kCountStride;
 
@@ -292,7 +299,10 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
   }
 
   if (tid <= kMaxRows) sh.acc[tid] = 0;
-  if (tid < kMaxRows) sh.lim[tid] = tid < R ? clamp_limit(c.limit, (int64_t)l * R + tid, N) : 0;
+  if (tid == 0) {
+#pragma unroll
+    for (int r = 0; r < kMaxRows; ++r) sh.lim[r] = s.lim[r];
+  }
 
   // admitted counts per row and for the union
   __syncthreads();
@@ -318,7 +328,7 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
       j0 = tid + (int64_t)kCountWords * kPrepThreads;
     }
     for (int64_t j = j0; j < words; j += kPrepThreads) {
-      rc[kMaxRows] += __popc(union_word(c, mask_l, s, j));
+      rc[kMaxRows] += __popc(union_word<R>(c, mask_l, s, j));
 #pragma unroll
       for (int r = 0; r < R; ++r) rc[r] += __popc(row_word(c, mask_l, s, r, j));
     }
@@ -382,9 +392,10 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
 }
 
 // Workgroup x >= 1 of layer l: expand tiles [16 (x-1), 16 x) of the union.
+template <int R>
 __device__ void expand_tiles(const Call& c, int l, int x, ExpandShared& sh) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const Limits s = layer_limits(c, l);
+  const Limits s = layer_limits<R>(c, l);
   const uint32_t* mask_l = c.mask + (int64_t)l * c.mask_layer_stride;
   const int64_t words = (s.maxlim + 31) / 32;
   const int t0 = (x - 1) * kPrepTilesPerWg;
@@ -392,12 +403,12 @@ __device__ void expand_tiles(const Call& c, int l, int x, ExpandShared& sh) {
   // this wave's tile word (loaded alongside the earlier tiles' words)
   const int t = t0 + wave;
   const int64_t j = (int64_t)t * kTileWords + lane;
-  const uint32_t u = (t < c.ntiles && j < words) ? union_word(c, mask_l, s, j) : 0u;
+  const uint32_t u = (t < c.ntiles && j < words) ? union_word<R>(c, mask_l, s, j) : 0u;
 
   // admitted blocks of all earlier tiles
   int before = 0;
   const int64_t w_end = (int64_t)t0 * kTileWords < words ? (int64_t)t0 * kTileWords : words;
-  for (int64_t jj = tid; jj < w_end; jj += kPrepThreads) before += __popc(union_word(c, mask_l, s, jj));
+  for (int64_t jj = tid; jj < w_end; jj += kPrepThreads) before += __popc(union_word<R>(c, mask_l, s, jj));
   if (tid == 0) sh.before = 0;
   __syncthreads();
   before = wave_sum(before);
@@ -429,7 +440,7 @@ template <int R, int D>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(Call c) {
   __shared__ PrepShared sh;
   if (blockIdx.x == 0) fold_count_floor<R, D>(c, blockIdx.y, sh.f);
-  else expand_tiles(c, blockIdx.y, blockIdx.x, sh.e);
+  else expand_tiles<R>(c, blockIdx.y, blockIdx.x, sh.e);
 }
 
 template <int R>

@@ -44,7 +44,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 16;                     // compacted entries per wave step
 constexpr int kWaves = kScoreThreads / kWave;  // 4
-constexpr int kPiece = kScorePieceMax;         // largest piece one workgroup streams
+constexpr int kPiece = kScorePieceMax + 2 * kGroup;  // largest piece one workgroup streams
+constexpr bool kInterleavedPieces = true;  // a piece is every P-th group of 16 positions
 
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
@@ -61,7 +62,7 @@ struct ScoreShared {
   int P[kMaxRows];
   int64_t lim[kMaxRows];
   uint32_t floor[kMaxRows];
-  int piece[3];
+  int piece[4];
   int wstaged[kWaves][kMaxRows];  // end of piece: each wave's staged count per row
   int base[kMaxRows];             // end of piece: the workgroup's slot in each row's list
 };
@@ -83,7 +84,8 @@ __device__ __forceinline__ void flush_staged(const uint64_t* stage, int n, int32
 // Per-wave candidate staging and the piece's context.
 template <int R>
 struct PieceCtx {
-  int off, cnt;                // positions [off, off + cnt) of the current layer
+  int off, cnt;                // elements [0, cnt); element e is position pos_of(e) of the layer
+  int pj, pn, nl;              // interleaved: piece j of pn, layer's admitted count nl
   int mode;
   const ScoreShared<R>* sh;
   uint64_t* stage;             // this wave's [R][kWaveCandBuf]
@@ -94,13 +96,21 @@ struct PieceCtx {
   const uint32_t* mask_l;      // the layer's mask rows (kRowMask)
   int64_t mask_row_stride;
 
-  __device__ __forceinline__ int block_of(int e) const {
-    return mode == kNoMask ? off + e : sh->list[e];
+  // Layer position of piece element e: contiguous pieces hold [off, off + cnt);
+  // interleaved piece j of pn holds groups j, j + pn, j + 2 pn, ... of 16.
+  __device__ __forceinline__ int pos_of(int e) const {
+    return kInterleavedPieces ? ((e >> 4) * pn + pj) * kGroup + (e & (kGroup - 1)) : off + e;
   }
 
-  // Is position off + e a candidate of row r with score s?  Sets its key.
+  __device__ __forceinline__ bool valid(int e) const { return e < cnt && pos_of(e) < nl; }
+
+  __device__ __forceinline__ int block_of(int e) const {
+    return mode == kNoMask ? pos_of(e) : sh->list[e];
+  }
+
+  // Is position pos_of(e) a candidate of row r with score s?  Sets its key.
   __device__ __forceinline__ bool want(int r, int e, float s, uint32_t* key) const {
-    const int pos = off + e;
+    const int pos = pos_of(e);
     if (e >= cnt || pos >= sh->P[r]) return false;
     if (mode == kRowMask) {  // the union list also holds blocks other rows admit
       const int b = sh->list[e];
@@ -128,7 +138,7 @@ struct PieceCtx {
     if (ok) {
       const int lane = lane_id();
       const uint64_t below = lane == 0 ? 0ull : (bal & (~0ull >> (kWave - lane)));
-      stage[r * kWaveCandBuf + staged[r] + __popcll(below)] = pack_candidate(key, off + e);
+      stage[r * kWaveCandBuf + staged[r] + __popcll(below)] = pack_candidate(key, pos_of(e));
     }
     staged[r] += n;
   }
@@ -168,7 +178,7 @@ struct MfmaEngine {
   __device__ __forceinline__ void load(const PieceCtx<R>& t, const uint16_t* K, int64_t ldk, int g0) {
     const int lane = lane_id();
     const int e = g0 + (lane & 15);
-    if (e < t.cnt) {
+    if (t.valid(e)) {
       const uint16_t* row = K + (int64_t)t.block_of(e) * ldk + 8 * (lane >> 4);
 #pragma unroll
       for (int cc = 0; cc < KC; ++cc) buf[B][cc] = load16(row + 32 * cc);
@@ -231,7 +241,7 @@ struct ValuEngine {
     for (int u = 0; u < U; ++u) {
       const int e = g0 + u * RPI + rr;
       buf[B][u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (e < t.cnt) buf[B][u] = load16(K + (int64_t)t.block_of(e) * ldk + slice * 8);
+      if (t.valid(e)) buf[B][u] = load16(K + (int64_t)t.block_of(e) * ldk + slice * 8);
     }
   }
 
@@ -311,7 +321,7 @@ __device__ __forceinline__ void stream_piece(Engine& eng, PieceCtx<Engine::kRows
 // than the grid, which the host sizes for full admission at T = 2048.  So a
 // usual call runs as one round of equal workgroups, and surplus ones exit.
 struct Piece {
-  int layer, s0, s1;  // positions [s0, s1) of the layer; layer < 0: nothing to do
+  int layer, j, pn, T;  // piece j of the pn pieces of `layer` (layer < 0: nothing to do)
 };
 
 __device__ Piece find_piece(const Call& c, int* shared_out) {
@@ -330,7 +340,7 @@ __device__ Piece find_piece(const Call& c, int* shared_out) {
     const int64_t per = div > 0 ? (total + div - 1) / div : kScorePieceMax;
     const int T = (int)(per < kScorePieceMin ? kScorePieceMin : (per > kScorePieceMax ? kScorePieceMax : per));
     const int j = blockIdx.x;
-    int base = 0, layer = -1, s0 = 0, nl = 0;
+    int base = 0, layer = -1, pj = 0, pn = 0;
     for (int l0 = 0; l0 < L && layer < 0; l0 += kWave) {
       const int l = l0 + lane;
       const int n = l < L ? c.counts[(int64_t)l * kCountStride + kMaxRows] : 0;
@@ -341,19 +351,20 @@ __device__ Piece find_piece(const Call& c, int* shared_out) {
       if (hit) {
         const int src = __ffsll((long long)hit) - 1;
         layer = l0 + src;
-        s0 = (j - (base + __shfl(incl - g, src, kWave))) * T;
-        nl = __shfl(n, src, kWave);
+        pj = j - (base + __shfl(incl - g, src, kWave));
+        pn = __shfl(g, src, kWave);
       }
       base += __shfl(incl, kWave - 1, kWave);
     }
     if (lane == 0) {
       shared_out[0] = layer;
-      shared_out[1] = s0;
-      shared_out[2] = layer < 0 ? 0 : (s0 + T < nl ? s0 + T : nl);
+      shared_out[1] = pj;
+      shared_out[2] = pn;
+      shared_out[3] = T;
     }
   }
   __syncthreads();
-  return Piece{shared_out[0], shared_out[1], shared_out[2]};
+  return Piece{shared_out[0], shared_out[1], shared_out[2], shared_out[3]};
 }
 
 template <int R, int D, class Engine>
@@ -363,14 +374,29 @@ __device__ __forceinline__ void score_body(const Call& c) {
   const int64_t N = c.blocks;
   const Piece pz = find_piece(c, sh.piece);
   if (pz.layer < 0) return;  // uniform for the workgroup
-  const int sl = pz.layer, s0 = pz.s0, s1 = pz.s1;
+  const int sl = pz.layer;
 
   // Set-up: one round of independent loads.
   const int32_t* counts = c.counts + (int64_t)sl * kCountStride;
   const int nl = counts[kMaxRows];
+  PieceCtx<R> pc;
+  pc.nl = nl;
+  pc.pj = pz.j;
+  pc.pn = pz.pn;
+  if (kInterleavedPieces) {
+    const int groups = (nl + kGroup - 1) / kGroup;
+    pc.off = 0;
+    pc.cnt = ((groups - pz.j + pz.pn - 1) / pz.pn) * kGroup;
+  } else {
+    pc.off = pz.j * pz.T;
+    pc.cnt = (pc.off + pz.T < nl ? pc.off + pz.T : nl) - pc.off;
+  }
   if (c.mode != kNoMask) {
-    const int32_t* list = c.list + (int64_t)sl * N + s0;
-    for (int i = tid; i < s1 - s0; i += kScoreThreads) sh.list[i] = list[i];
+    const int32_t* list = c.list + (int64_t)sl * N;
+    for (int i = tid; i < pc.cnt; i += kScoreThreads) {
+      const int pos = pc.pos_of(i);
+      sh.list[i] = pos < nl ? list[pos] : 0;
+    }
   }
   if (tid < kMaxRows) {
     sh.P[tid] = tid < R ? (c.mode == kRowMask ? nl : counts[tid]) : 0;
@@ -382,9 +408,6 @@ __device__ __forceinline__ void score_body(const Call& c) {
   eng.init(c, sl);
   __syncthreads();
 
-  PieceCtx<R> pc;
-  pc.off = s0;
-  pc.cnt = s1 - s0;
   pc.mode = c.mode;
   pc.sh = &sh;
   pc.stage = &sh.stage[wave][0][0];

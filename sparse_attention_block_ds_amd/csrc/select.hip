@@ -12,13 +12,13 @@
 // block index, so one unsigned compare is the whole output order, ties to the
 // lower block index included.
 //
-// One workgroup per (layer, row), m = min(k, admitted):
+// One workgroup of NT threads per (layer, row), m = min(k, admitted):
 //  * Usual path: the score kernel left c candidates, every key at or above the
 //    row's floor.  If c >= m the best m of the row are among them (at least m
 //    keys reach the floor, so the m-th best does, and so do all its ties).  A
 //    radix select over the candidate words (in registers when c <= 8192, else
-//    re-read from memory on each pass) narrows them to at most max(m, 1024),
-//    whose best m are placed in descending order.
+//    re-read from memory on each pass) narrows them to at most m + 64, whose
+//    best m are placed in descending order.
 //  * Exact fallback (c < m: the floor was set too high): the row is rescored
 //    in fp32 over every admitted position, its words replace the candidate
 //    list, and the same select runs over all of them.
@@ -33,37 +33,11 @@
 namespace dssel {
 namespace {
 
-constexpr int NT = kSelectThreads;
-constexpr int kWaves = NT / kWave;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ uint64_t pack(uint32_t key, int pos) {
   return ((uint64_t)key << 32) | (uint32_t)~(uint32_t)pos;
 }
 __device__ __forceinline__ uint32_t key_of(uint64_t e) { return (uint32_t)(e >> 32); }
 __device__ __forceinline__ int pos_of(uint64_t e) { return (int)~(uint32_t)e; }
-
-// Largest bin B in [0, nbins) with (keys in bins >= B) >= need, and the
-// number of keys in bins > B.  nbins is 1024 or 2048; the histogram is in LDS.
-__device__ void find_boundary(const uint32_t* hist, int nbins, int need, int* out_bin,
-                              int* out_above, int* scan_scratch) {
-  const int per = nbins / NT;  // 1 or 2 bins per thread, in descending bin order
-  const int hi = nbins - 1 - threadIdx.x * per;
-  const int c_hi = (int)hist[hi];
-  const int c_lo = per == 2 ? (int)hist[hi - 1] : 0;
-  int total = 0;
-  const int excl = block_exclusive_scan<NT>(c_hi + c_lo, &total, scan_scratch);
-  if (excl < need && excl + c_hi + c_lo >= need) {
-    if (excl + c_hi >= need) {
-      *out_bin = hi;
-      *out_above = excl;
-    } else {
-      *out_bin = hi - 1;
-      *out_above = excl + c_hi;
-    }
-  }
-  __syncthreads();
-}
 
 constexpr int kRun = kWave;  // words per sorted run: one per lane of a wave
 
@@ -81,15 +55,59 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// LDS words: the gathered words (at most 2 NT) with a run of zero padding,
+// then the best m in order (m <= k <= DS_SEL_MAX_K = 2048).
+constexpr int kGatherMax = 2048 + kGatherSlack;  // the most words gathered: k <= 2048, plus slack
+constexpr int kGatherCap = kGatherMax + kRun;
+constexpr int kOrderedCap = 2048;
+
+// Everything that depends on the workgroup size NT (threads per row).
+template <int NT>
+struct SelectT {
+  static constexpr int kWaves = NT / kWave;
+
+struct Shared {
+  uint32_t hist[kHistBins];
+  uint64_t se[kGatherCap + kOrderedCap];  // [0, kGatherCap): gathered; then the best m, sorted
+  float q[256];
+  int scan[kWaves + 1];
+  int bin, above, count;
+};
+
+// Largest bin B in [0, nbins) with (keys in bins >= B) >= need, and the
+// number of keys in bins > B.  nbins is 1024 or 2048; the histogram is in LDS.
+static __device__ void find_boundary(const uint32_t* hist, int nbins, int need, int* out_bin,
+                              int* out_above, int* scan_scratch) {
+  const int per = nbins / NT;  // bins per thread, taken in descending order
+  const int hi = nbins - 1 - threadIdx.x * per;
+  int mine = 0;
+  for (int i = 0; i < per; ++i) mine += (int)hist[hi - i];
+  int total = 0;
+  const int excl = block_exclusive_scan<NT>(mine, &total, scan_scratch);
+  if (excl < need && excl + mine >= need) {
+    int above = excl;
+    for (int i = 0; i < per; ++i) {
+      const int cnt = (int)hist[hi - i];
+      if (above + cnt >= need) {
+        *out_bin = hi - i;
+        *out_above = above;
+        break;
+      }
+      above += cnt;
+    }
+  }
+  __syncthreads();
+}
+
 // The best m of the n distinct words se[0, n), in descending order, into
 // out[0, min(n, m)).  The words are cut into runs of 64; each wave sorts runs
 // in registers (a bitonic network across its lanes), and a word's place is
 // the number of larger words, summed over the runs by a binary search in
 // each.  se[n, 64 * ceil(n / 64)) must hold zero words, which are never larger
 // than a candidate.
-__device__ void sort_place(uint64_t* se, int n, int m, uint64_t* out) {
+static __device__ void sort_place(uint64_t* se, int n, int m, uint64_t* out) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int runs = (n + kRun - 1) / kRun;  // <= 2 NT / 64 = 32
+  const int runs = (n + kRun - 1) / kRun;  // <= kGatherCap / 64 = 34
   for (int run = wave; run < runs; run += NT / kWave) {
     uint64_t v = se[run * kRun + lane];
     for (int k = 2; k <= kRun; k <<= 1)
@@ -120,26 +138,33 @@ __device__ void sort_place(uint64_t* se, int n, int m, uint64_t* out) {
   __syncthreads();
 }
 
-constexpr int kGatherCap = kSelectBuf / 2;  // gathered words; the sorted best m follow them
-
-struct SelectShared {
-  uint32_t hist[kHistBins];
-  uint64_t se[kSelectBuf];  // [0, kGatherCap): gathered words; [kGatherCap, ...): the best m, sorted
-  float q[256];
-  int scan[kWaves + 1];
-  int bin, above, count;
-};
-
 // Candidate words held in registers, at most kPer per thread (c <= kSelectBuf).
+// The loads do not wait for the count: every slot below min(kSelectBuf, cap)
+// lies inside the row's list (which has room for every position), and the
+// slots at or past c are simply never used.
 struct RegisterWords {
   static constexpr int kPer = kSelectBuf / NT;
   uint64_t v[kPer];
-  int c;
-  __device__ RegisterWords(const uint64_t* src, int count) : c(count) {
+  int c = 0;
+  // The first half of the slots, before the count is known (the usual lists
+  // hold 2,000-4,000 words) ...
+  __device__ void load_head(const uint64_t* src, int64_t cap) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
+    for (int u = 0; u < kPer / 2; ++u) {
       const int i = u * NT + (int)threadIdx.x;
-      v[u] = i < c ? src[i] : 0ull;
+      v[u] = i < cap ? src[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = kPer / 2; u < kPer; ++u) v[u] = 0ull;
+  }
+  // ... and the rest once it is, only if it needs them.
+  __device__ void load_tail(const uint64_t* src, int count) {
+    if (count > (kPer / 2) * NT) {
+#pragma unroll
+      for (int u = kPer / 2; u < kPer; ++u) {
+        const int i = u * NT + (int)threadIdx.x;
+        v[u] = i < count ? src[i] : 0ull;
+      }
     }
   }
   template <class F>
@@ -172,9 +197,9 @@ struct GlobalWords {
 // (one per position), so six passes always suffice; on the usual candidate
 // lists one or two are needed.
 template <class Words>
-__device__ void radix_select_words(const Words& src, int c, int m, SelectShared& sh) {
+static __device__ void radix_select_words(const Words& src, int c, int m, Shared& sh) {
   const int tid = threadIdx.x;
-  const int gather_max = m + kGatherSlack < 2 * NT ? m + kGatherSlack : 2 * NT;  // >= m
+  const int gather_max = m + kGatherSlack;  // <= kGatherMax
   int pbits = 0;
   uint64_t prefix = 0;
   int above = 0, in_range = c, need = m;
@@ -205,8 +230,8 @@ __device__ void radix_select_words(const Words& src, int c, int m, SelectShared&
     const int slot = wave_append(want, &sh.count);
     if (want && slot < kGatherCap) sh.se[slot] = w;
   });
-  int gathered = above + in_range;  // <= gather_max <= 2 NT
-  gathered = gathered < 2 * NT ? gathered : 2 * NT;
+  int gathered = above + in_range;  // <= gather_max <= kGatherMax
+  gathered = gathered < kGatherMax ? gathered : kGatherMax;
   if (tid < kRun) sh.se[gathered + tid] = 0ull;
   __syncthreads();
   sort_place(sh.se, gathered, m, sh.se + kGatherCap);
@@ -215,7 +240,7 @@ __device__ void radix_select_words(const Words& src, int c, int m, SelectShared&
 // Exact fallback: the floor let fewer than m keys through, so row (l, r) is
 // rescored in fp32 over every admitted position and its words replace the
 // candidate list.
-__device__ int rescore_row(const Call& c, int l, int r, uint64_t* words, SelectShared& sh) {
+static __device__ int rescore_row(const Call& c, int l, int r, uint64_t* words, Shared& sh) {
   const int tid = threadIdx.x;
   const int R = c.rows, D = c.dim;
   const int64_t N = c.blocks, lr = (int64_t)l * R + r;
@@ -261,25 +286,37 @@ __device__ int rescore_row(const Call& c, int l, int r, uint64_t* words, SelectS
   return sh.count;
 }
 
-__global__ __launch_bounds__(NT) void select_kernel(Call c) {
-  __shared__ SelectShared sh;
+static __device__ void run(const Call& c, Shared& sh) {
   const int l = blockIdx.y, r = blockIdx.x;
   const int R = c.rows, k = c.k;
   const int64_t lr = (int64_t)l * R + r;
   const int64_t N = c.blocks;
-  const int n_adm = N ? c.counts[(int64_t)l * kCountStride + r] : 0;
+  // One round of independent loads: the counts and the candidate words.
+  const int32_t* cnt_l = c.counts + (int64_t)l * kCountStride;
+  const int n_adm = cnt_l[r];
+  const int n_union = cnt_l[kMaxRows];
+  int cands = c.cand_count[lr * kCountPad];
+  uint64_t* words = c.cand + lr * c.cand_stride;
+  RegisterWords rw;
+  rw.load_head(words, c.cand_stride);
   const int m = n_adm < k ? n_adm : k;
-  const int P = c.mode == kRowMask ? (N ? c.counts[(int64_t)l * kCountStride + kMaxRows] : 0) : n_adm;
+  const int P = c.mode == kRowMask ? n_union : n_adm;
   int32_t* oi = c.out_idx + lr * k;
   float* os = c.out_score + lr * k;
   const int tid = threadIdx.x;
 
   if (m > 0) {
-    uint64_t* words = c.cand + lr * c.cand_stride;
-    int cands = c.cand_count[lr * kCountPad];
-    if (cands < m) cands = rescore_row(c, l, r, words, sh);
-    if (cands <= kSelectBuf) radix_select_words(RegisterWords(words, cands), cands, m, sh);
-    else radix_select_words(GlobalWords{words, cands}, cands, m, sh);
+    if (cands < m) {
+      cands = rescore_row(c, l, r, words, sh);
+      rw.load_head(words, c.cand_stride);
+    }
+    if (cands <= kSelectBuf) {
+      rw.load_tail(words, cands);
+      rw.c = cands;
+      radix_select_words(rw, cands, m, sh);
+    } else {
+      radix_select_words(GlobalWords{words, cands}, cands, m, sh);
+    }
   }
 
   const int32_t* list = c.list + (int64_t)l * N;
@@ -298,11 +335,28 @@ __global__ __launch_bounds__(NT) void select_kernel(Call c) {
   if (tid == 0 && c.out_count) c.out_count[lr] = m;
 }
 
+};
+
+template <int NT>
+__global__ __launch_bounds__(NT) void select_kernel(Call c) {
+  __shared__ typename SelectT<NT>::Shared sh;
+  SelectT<NT>::run(c, sh);
+}
+
 }  // namespace
 
 hipError_t launch_select(const Call& c, hipStream_t stream) {
+  // One workgroup per (layer, row).  A 1,024-thread workgroup is fastest for a
+  // row, but only one is resident per compute unit; when the rows outnumber
+  // the compute units, 512-thread workgroups (two per unit) keep every row in
+  // one round.
+  const int64_t rows = (int64_t)c.layers * c.rows;
+  const int64_t cus = c.score_slots / kScoreWgsPerCu;
   dim3 grid(c.rows, c.layers);
-  hipLaunchKernelGGL(select_kernel, grid, dim3(kSelectThreads), 0, stream, c);
+  if (rows > cus)
+    hipLaunchKernelGGL(select_kernel<512>, grid, dim3(512), 0, stream, c);
+  else
+    hipLaunchKernelGGL(select_kernel<1024>, grid, dim3(1024), 0, stream, c);
   return hipGetLastError();
 }
 

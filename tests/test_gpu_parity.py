@@ -166,6 +166,17 @@ def test_general_custom(selector, values, mask_p, shared):
     gs.assert_general(p, gpu, gs.run_oracle(p))
 
 
+@pytest.mark.parametrize("k", [512, 2048])
+def test_more_rows_than_compute_units(selector, k):
+    """43 x 8 = 344 selections: more than one per compute unit, so the select
+    runs with its smaller workgroups; large k exercises their widest order."""
+    p = wl.make_custom(43, 8, 8, 64, 3000, k, seed=310 + k, values="int3", mask_p=0.7)
+    _print_case(f"many_rows_k{k}", p)
+    gpu = gs.run_gpu(selector, p)
+    gs.assert_self_consistent(p, gpu)
+    gs.assert_bit_exact(gpu, gs.run_oracle(p), f"many_rows_k{k}")
+
+
 def test_repeated_calls_identical(selector):
     """Atomic append order must not leak into the output (tie-heavy input)."""
     import torch
