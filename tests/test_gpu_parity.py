@@ -190,6 +190,32 @@ def test_repeated_calls_identical(selector):
     torch.cuda.synchronize()
 
 
+def test_graph_capture_replays(selector):
+    """The whole call captured once into a HIP graph (one submission for all layers)
+    replays to the eager result, with other work and synchronisations in between."""
+    import torch
+    p = wl.make_custom(4, 6, 16, 128, 9000, 512, seed=320, values="int3", mask_p=0.6,
+                       limits=np.array([[9000 - 5 + r for r in range(6)]] * 4))
+    q, w, keys, mask, limit = sel.upload(p)
+    eager = [t.clone() for t in selector.score_select(q, w, keys, p.k, mask, limit)]
+    torch.cuda.synchronize()
+    out = tuple(torch.full_like(t, -7) for t in eager)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        selector.score_select(q, w, keys, p.k, mask, limit, out=out)
+    for i in range(3):
+        for t in out:
+            t.fill_(-7)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        for a, b in zip(eager, out):
+            assert torch.equal(a, b), f"replay {i}"
+    gs.assert_bit_exact(tuple(t.cpu().numpy() for t in out), gs.run_oracle(p), "graph")
+
+
 def test_capacity_error_leaves_outputs_untouched(selector):
     import torch
     p = wl.make_custom(1, 2, 8, 64, 80000, 16, seed=301, values="int3")
