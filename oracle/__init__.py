@@ -13,6 +13,10 @@ whole context, only mask-admitted blocks are candidates, the admitted index is
 built per row, the top 512 are kept).  The score formula, the order and the
 padding are readings of this library, stated in the C file's header.
 
+``attend`` is the step after the selection, read the same way: per attention
+head, the softmax over the selected blocks of scale * (q . K[b]) applied to the
+blocks' values V[b], in double precision (the C file states the reading).
+
 Every array is host numpy; bf16 values travel as their uint16 bit patterns.
 """
 from __future__ import annotations
@@ -50,6 +54,9 @@ def _declare(lib):
     lib.ds_sel_oracle_score_blocks.restype = ctypes.c_int
     lib.ds_sel_oracle_score_blocks.argtypes = [i32, i32, i32, i32, i64, p, p, p, i64, i64, i32,
                                                i32, i64, p, p]
+    lib.ds_sel_oracle_attend.restype = ctypes.c_int
+    lib.ds_sel_oracle_attend.argtypes = [i32, i32, i32, i32, i64, i32, p, p, i64, i64, p, i64, i64,
+                                         p, p, ctypes.c_double, p]
     return lib
 
 
@@ -137,4 +144,31 @@ def score_blocks(q, w, keys, layer, row, blocks_list, lib=None):
                                         _ptr(lst), _ptr(out))
     if rc != 0:
         raise OracleError(f"ds_sel_oracle_score_blocks returned {rc}")
+    return out
+
+
+def attend(qa, keys, values, idx, count, scale, lib=None):
+    """Attention over the selected blocks, in double precision.
+
+    qa     uint16 [L][R][Ha][d]  bf16 bits (attention query heads)
+    keys   uint16 [L][N][ldk]    bf16 bits (the block keys the selection scores)
+    values uint16 [L][N][ldv]    bf16 bits
+    idx    int32 [L][R][k]       selected blocks; entries past count are not read
+    count  int32 [L][R]
+    Returns out float64 [L][R][Ha][d]: per head, the softmax over the selected
+    blocks of scale * (q . K[b]) applied to V[b]; zero where count is 0.
+    """
+    qa, keys, values = _c(qa, np.uint16), _c(keys, np.uint16), _c(values, np.uint16)
+    idx, count = _c(idx, np.int32), _c(count, np.int32)
+    layers, rows, heads, dim = qa.shape
+    blocks, ldk, ldv, k = keys.shape[1], keys.shape[2], values.shape[2], idx.shape[2]
+    if keys.shape[0] != layers or values.shape[:2] != keys.shape[:2] or idx.shape[:2] != (layers, rows):
+        raise ValueError("inconsistent shapes")
+    out = np.empty((layers, rows, heads, dim), np.float64)
+    lib = lib or load()
+    rc = lib.ds_sel_oracle_attend(layers, rows, heads, dim, blocks, k, _ptr(qa), _ptr(keys), ldk,
+                                  blocks * ldk, _ptr(values), ldv, blocks * ldv, _ptr(idx),
+                                  _ptr(count), float(scale), _ptr(out))
+    if rc != 0:
+        raise OracleError(f"ds_sel_oracle_attend returned {rc}")
     return out

@@ -209,3 +209,76 @@ int ds_sel_oracle_score_blocks(int32_t layers, int32_t rows, int32_t heads, int3
   }
   return ORACLE_OK;
 }
+
+/*
+ * Attention over the selected blocks -- the step that consumes the selection.
+ *
+ * Page "DeepSeek V4.1F Q4 on M3 Ultra with native DSpark MTP (40tps /
+ * 800tps)", paragraph "Decode at depth": the compressed attention of a layer
+ * attends to the 512 blocks the selection keeps.  The pages give no formula;
+ * the reading taken here is ordinary scaled-dot-product attention over the
+ * selected blocks, with the block key K[b] (the same key the selection
+ * scores) and a block value V[b]:
+ *   for each layer l, row r and attention head h, with c = count[l][r],
+ *     s_j = scale * (qa[l][r][h] . K[l][idx[l][r][j]])         j < c
+ *     o[l][r][h] = sum_j exp(s_j - max_i s_i) V[l][idx_j] / sum_j exp(s_j - max_i s_i)
+ *   and o = 0 when c = 0.
+ * Everything runs in double precision (bf16 inputs widen exactly); entries of
+ * idx at or past count are not read.  Returns ORACLE_E_INVALID when a read
+ * index lies outside [0, N).
+ */
+int ds_sel_oracle_attend(int32_t layers, int32_t rows, int32_t heads, int32_t dim, int64_t blocks,
+                         int32_t k, const uint16_t* qa, const uint16_t* keys, int64_t ldk,
+                         int64_t key_layer_stride, const uint16_t* values, int64_t ldv,
+                         int64_t value_layer_stride, const int32_t* idx, const int32_t* count,
+                         double scale, double* out) {
+  if (layers < 1 || rows < 1 || heads < 1 || dim < 1 || blocks < 0 || k < 1 || !qa || !idx ||
+      !count || !out || ldk < dim || ldv < dim)
+    return ORACLE_E_INVALID;
+  double* s = (double*)malloc(sizeof(double) * (size_t)k);
+  if (!s) return ORACLE_E_NOMEM;
+  for (int32_t l = 0; l < layers; ++l) {
+    const uint16_t* K = keys + (int64_t)l * key_layer_stride;
+    const uint16_t* V = values + (int64_t)l * value_layer_stride;
+    for (int32_t r = 0; r < rows; ++r) {
+      const int64_t lr = (int64_t)l * rows + r;
+      const int32_t* sel = idx + lr * k;
+      int32_t c = count[lr];
+      if (c < 0 || c > k) {
+        free(s);
+        return ORACLE_E_INVALID;
+      }
+      for (int32_t j = 0; j < c; ++j) {
+        if (sel[j] < 0 || (int64_t)sel[j] >= blocks) {
+          free(s);
+          return ORACLE_E_INVALID;
+        }
+      }
+      for (int32_t h = 0; h < heads; ++h) {
+        const uint16_t* qh = qa + (lr * heads + h) * (int64_t)dim;
+        double* oh = out + (lr * heads + h) * (int64_t)dim;
+        for (int32_t i = 0; i < dim; ++i) oh[i] = 0.0;
+        if (c == 0) continue;
+        double smax = -INFINITY;
+        for (int32_t j = 0; j < c; ++j) {
+          const uint16_t* kb = K + (int64_t)sel[j] * ldk;
+          double dot = 0.0;
+          for (int32_t i = 0; i < dim; ++i)
+            dot += (double)bf16_bits_to_float(qh[i]) * (double)bf16_bits_to_float(kb[i]);
+          s[j] = scale * dot;
+          if (s[j] > smax) smax = s[j];
+        }
+        double z = 0.0;
+        for (int32_t j = 0; j < c; ++j) {
+          const double p = exp(s[j] - smax);
+          const uint16_t* vb = V + (int64_t)sel[j] * ldv;
+          for (int32_t i = 0; i < dim; ++i) oh[i] += p * (double)bf16_bits_to_float(vb[i]);
+          z += p;
+        }
+        for (int32_t i = 0; i < dim; ++i) oh[i] /= z;
+      }
+    }
+  }
+  free(s);
+  return ORACLE_OK;
+}

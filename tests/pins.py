@@ -17,6 +17,8 @@ checks against deliberately broken copies of the oracle.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 import oracle
@@ -244,6 +246,97 @@ def check_metamorphic(lib):
         np.testing.assert_array_equal(x, y)
 
 
+# ------------------------------------------------------------------ attention
+def _bits(a):
+    return wl.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+
+def _attend(lib, qa, keys, values, idx, count, scale):
+    return oracle.attend(_bits(qa), _bits(keys), _bits(values), np.asarray(idx, np.int32),
+                         np.asarray(count, np.int32), scale, lib=lib)
+
+
+def check_attend(lib):
+    """Closed forms for the attention over the selected blocks (no retyped softmax)."""
+    rng = np.random.default_rng(40)
+    N, d, H, k = 300, 64, 3, 16
+    keys = rng.integers(-3, 4, (1, N, d)).astype(np.float32)
+    values = rng.integers(-3, 4, (1, N, d)).astype(np.float32)
+    qa = rng.integers(-3, 4, (1, 1, H, d)).astype(np.float32)
+    idx = np.full((1, 1, k), -1, np.int32)
+
+    # one selected block: every head returns exactly that block's value row
+    idx[0, 0, 0] = 123
+    out = _attend(lib, qa, keys, values, idx, [[1]], 0.7)
+    for h in range(H):
+        assert np.array_equal(out[0, 0, h], values[0, 123].astype(np.float64)), "single block"
+
+    # scale 0: the exact mean of the selected value rows
+    sel = rng.choice(N, 10, replace=False)
+    idx[0, 0, :10] = sel
+    out = _attend(lib, qa, keys, values, idx, [[10]], 0.0)
+    exact = values[0, sel].astype(np.float64).sum(axis=0) / 10
+    assert np.allclose(out[0, 0, 0], exact, rtol=0, atol=1e-12), "scale 0 is the mean"
+
+    # one block dominates by 1024: its value row exactly (other weights underflow to 0)
+    kd = np.zeros((1, N, d), np.float32)
+    kd[0, sel[3], 0] = 8.0
+    qd = np.zeros((1, 1, 1, d), np.float32)
+    qd[0, 0, 0, 0] = 1.0
+    out = _attend(lib, qd, kd, values, idx, [[10]], 128.0)
+    assert np.array_equal(out[0, 0, 0], values[0, sel[3]].astype(np.float64)), "dominant block"
+
+    # two blocks: o = V2 + (V1 - V2) * logistic(s1 - s2)
+    k2 = np.zeros((1, N, d), np.float32)
+    k2[0, 10, 0], k2[0, 20, 0] = 3.0, 1.0
+    i2 = np.full((1, 1, k), -1, np.int32)
+    i2[0, 0, :2] = [10, 20]
+    out = _attend(lib, qd, k2, values, i2, [[2]], 0.5)
+    sig = 1.0 / (1.0 + math.exp(-(1.5 - 0.5)))
+    v1, v2 = values[0, 10].astype(np.float64), values[0, 20].astype(np.float64)
+    assert np.allclose(out[0, 0, 0], v2 + (v1 - v2) * sig, rtol=0, atol=1e-13), "two blocks"
+
+    # the order of the selected list does not matter; entries past count are not read
+    kn = rng.normal(size=(1, N, d)).astype(np.float32)
+    sel = rng.choice(N, k, replace=False).astype(np.int32)
+    base = _attend(lib, qa, kn, values, sel[None, None, :], [[k]], 0.125)
+    perm = rng.permutation(k)
+    assert np.allclose(_attend(lib, qa, kn, values, sel[perm][None, None, :], [[k]], 0.125), base,
+                       rtol=1e-12, atol=1e-12), "permutation"
+    padded = sel.copy()
+    padded[12:] = 7 * N  # past count 12: never read
+    short = _attend(lib, qa, kn, values, padded[None, None, :], [[12]], 0.125)
+    ref12 = _attend(lib, qa, kn, values, sel[None, None, :], [[12]], 0.125)
+    assert np.array_equal(short, ref12), "entries past count"
+
+    # heads, rows and layers are independent problems
+    for h in range(H):
+        one = _attend(lib, qa[:, :, h:h + 1], kn, values, sel[None, None, :], [[k]], 0.125)
+        assert np.array_equal(one[0, 0, 0], base[0, 0, h]), "head independence"
+    q2 = rng.integers(-3, 4, (2, 2, 2, d)).astype(np.float32)
+    k2l = rng.normal(size=(2, N, d)).astype(np.float32)
+    v2l = rng.integers(-3, 4, (2, N, d)).astype(np.float32)
+    i2l = np.stack([np.stack([rng.choice(N, k, replace=False) for _ in range(2)]) for _ in range(2)])
+    c2l = np.array([[k, 5], [0, 9]], np.int32)
+    both = _attend(lib, q2, k2l, v2l, i2l, c2l, 0.25)
+    for l in range(2):
+        for r in range(2):
+            one = _attend(lib, q2[l:l + 1, r:r + 1], k2l[l:l + 1], v2l[l:l + 1], i2l[l:l + 1, r:r + 1],
+                          c2l[l:l + 1, r:r + 1], 0.25)
+            assert np.array_equal(one[0, 0], both[l, r]), "layer/row independence"
+    assert not both[1, 0].any(), "count 0 gives zeros"
+
+    # an index outside [0, N) within count is rejected
+    bad = sel.copy()
+    bad[0] = N
+    try:
+        _attend(lib, qa, kn, values, bad[None, None, :], [[k]], 0.125)
+    except oracle.OracleError:
+        pass
+    else:
+        raise AssertionError("out-of-range index accepted")
+
+
 def all_pins(lib, include_slow=False):
     """Every pin; raises AssertionError on the first failure."""
     check_exact_integer(wl.make_custom(1, 1, 4, 64, 1500, 512, seed=0, values="int3"), lib)
@@ -260,5 +353,6 @@ def all_pins(lib, include_slow=False):
                                     mask_p=0.5), lib)
     check_special_cases(lib)
     check_metamorphic(lib)
+    check_attend(lib)
     if include_slow:
         check_exact_integer(wl.make("tiny"), lib)

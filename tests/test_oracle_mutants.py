@@ -29,6 +29,11 @@ MUTANTS = [
     ("wrong_row_of_w", "const uint16_t* w_row = w + lr * heads;", "const uint16_t* w_row = w + (int64_t)l * rows * heads;"),
     ("shared_mask_ignores_row", "mask + l * mask_layer_stride + r * mask_row_stride",
      "mask + l * mask_layer_stride"),
+    ("attend_no_max_shift", "const double p = exp(s[j] - smax);", "const double p = exp(s[j]);"),
+    ("attend_value_of_slot", "V + (int64_t)sel[j] * ldv", "V + (int64_t)j * ldv"),
+    ("attend_key_of_slot", "K + (int64_t)sel[j] * ldk", "K + (int64_t)j * ldk"),
+    ("attend_no_scale", "s[j] = scale * dot;", "s[j] = dot;"),
+    ("attend_divide_by_count", "oh[i] /= z;", "oh[i] /= c;"),
 ]
 
 
