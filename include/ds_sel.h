@@ -145,6 +145,55 @@ int ds_sel_score_select(ds_sel* h, const ds_sel_args* a, void* hip_stream);
 int ds_sel_score_select_profiled(ds_sel* h, const ds_sel_args* a, void* hip_stream,
                                  void* const events[4]);
 
+/* Attention over a selection -- the step that consumes it (page "DeepSeek
+ * V4.1F Q4 on M3 Ultra with native DSpark MTP (40tps / 800tps)", paragraph
+ * "Decode at depth": each layer's compressed attention works on the blocks
+ * the selection keeps; paragraph "Prefill": the attention core).  The pages
+ * give no formula.  This library defines, for layer l, row r and attention
+ * head h, with c = clamp(count[l][r], 0, k) (count NULL -> k) and S the slots
+ * j < c whose index idx[l][r][j] lies in [0, N):
+ *
+ *   s_j        = scale * (q[l][r][h][:] . K[l][idx_j][:])   bf16 inputs, fp32 sums
+ *   out[l][r][h] = sum_{j in S} exp(s_j - max s) V[l][idx_j] / sum_{j in S} exp(s_j - max s)
+ *
+ * and out = 0 when S is empty.  Slots outside S are skipped, never read: the
+ * padding (-1) that ds_sel_score_select writes past its count is one such
+ * slot, so its outputs can be passed here unchanged.  The weights are carried
+ * to about 2^-17 relative; everything else is fp32.  Element strides. */
+typedef struct {
+  uint32_t struct_size; /* sizeof(ds_sel_attend_args) */
+  int32_t layers;       /* L >= 1 */
+  int32_t rows;         /* R, 1 .. DS_SEL_MAX_ROWS */
+  int32_t heads;        /* attention heads Ha, 1 .. DS_SEL_MAX_HEADS */
+  int32_t dim;          /* d in {32, 64, 128, 256} */
+  int32_t k;            /* slots per (l, r) in idx, 1 .. max_k */
+  float scale;          /* finite; 1/sqrt(d) is the usual choice */
+  int32_t reserved;     /* 0 */
+  int64_t blocks;       /* N >= 0: indices at or above N are skipped */
+  const void* q;        /* bf16 [L][R][Ha][d], contiguous, 16-byte aligned */
+  const void* keys;     /* bf16; block b of layer l at keys + l*key_layer_stride + b*ldk;
+                           16-byte aligned; may be NULL only when N == 0 */
+  int64_t ldk;          /* >= d, multiple of 8 */
+  int64_t key_layer_stride; /* multiple of 8; >= N*ldk when L > 1 */
+  const void* values;   /* bf16, laid out like keys with ldv and value_layer_stride */
+  int64_t ldv;          /* >= d, multiple of 8 */
+  int64_t value_layer_stride; /* multiple of 8; >= N*ldv when L > 1 */
+  const int32_t* idx;   /* int32 [L][R][k] */
+  const int32_t* count; /* int32 [L][R], or NULL (all k slots) */
+  float* out;           /* fp32 [L][R][Ha][d] */
+} ds_sel_attend_args;
+
+/* Enqueue attention over a selection on `hip_stream`, as ds_sel_score_select
+ * does (same handle, stream rules and status codes).  The handle's capacity
+ * bounds layers, rows, heads (attention heads here), dim, k and blocks.  When
+ * few (layer, row) pairs are given, each pair's selection is split across
+ * several workgroups, whose partial results sit in the handle's scratch and
+ * are merged by a second kernel. */
+int ds_sel_attend(ds_sel* h, const ds_sel_attend_args* a, void* hip_stream);
+
+/* The host-side checks ds_sel_attend applies, without a device. */
+int ds_sel_check_attend_args(const ds_sel_limits* lim, const ds_sel_attend_args* a);
+
 /* Free the handle and its scratch (waits for the device to finish using it).
  * NULL is a no-op. */
 void ds_sel_destroy(ds_sel* h);
@@ -159,8 +208,9 @@ int ds_sel_check_args(const ds_sel_limits* lim, const ds_sel_args* a);
  * each part rounded up to 256 bytes: the folded query (L R D fp32), its three
  * bf16 parts (3 L R D), the compacted admitted index (L N int32), per-layer
  * counts (9 L int32), candidate floors (L R uint32), candidate counters one
- * per 128 bytes (32 L R int32), and candidate lists with room for every
- * position (L R ceil4(N) uint64). */
+ * per 128 bytes (32 L R int32), candidate lists with room for every
+ * position (L R ceil4(N) uint64), and the attention's split records
+ * (512 records of 64 heads, each a max and a sum plus D fp32). */
 int64_t ds_sel_scratch_bytes(const ds_sel_limits* lim);
 
 /* A static string naming a status code. */

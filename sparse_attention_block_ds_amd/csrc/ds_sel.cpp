@@ -3,6 +3,7 @@
 // score -> select) on the caller's stream without synchronising.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <new>
 
 #include "ds_sel.h"
@@ -15,11 +16,13 @@ struct ds_sel {
   int compute_units = 256;  // of the handle's device, read at create
   // offsets into scratch
   int64_t off_qt = 0, off_qparts = 0, off_list = 0, off_counts = 0, off_floor = 0, off_ccount = 0,
-          off_cand = 0;
+          off_cand = 0, off_part_ml = 0, off_part_o = 0;
 };
 
 // The select orders at most 2048 winners per row in LDS.
 static_assert(DS_SEL_MAX_K <= 2048, "select kernel LDS sized for k <= 2048");
+static_assert(DS_SEL_MAX_K <= dssel::kAttendMaxK, "attention kernel LDS sized for k <= kAttendMaxK");
+static_assert(DS_SEL_MAX_DIM <= 256, "attention kernels built for d <= 256");
 
 namespace {
 
@@ -28,13 +31,15 @@ constexpr int64_t kAlign = 256;
 int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  int64_t qt, qparts, list, counts, floor, ccount, cand, total;
+  int64_t qt, qparts, list, counts, floor, ccount, cand, part_ml, part_o, total;
 };
 
 // Scratch for a capacity: q~ fp32 [L][R][d] and its bf16 parts [L][3][R][d],
 // compacted index int32 [L][N], counts int32 [L][9], candidate floors uint32
 // [L][R], candidate counts int32 [L][R] (one per 128 bytes), and candidate words uint64
-// [L][R][N rounded up to 4] (room for every position, so none is ever dropped).
+// [L][R][N rounded up to 4] (room for every position, so none is ever dropped);
+// then the attention's split records: (max, sum) and o[d] fp32 per head of a
+// 64-head tile, for at most kAttendPartialWgs workgroups.
 Layout layout_for(const ds_sel_limits& lim) {
   Layout s{};
   const int64_t L = lim.max_layers, R = lim.max_rows, D = lim.max_dim, N = lim.max_blocks;
@@ -46,6 +51,9 @@ Layout layout_for(const ds_sel_limits& lim) {
   s.floor = off;  off += align_up(L * R * 4);
   s.ccount = off; off += align_up(L * R * dssel::kCountPad * 4);
   s.cand = off;   off += align_up(L * R * ((N + 3) / 4 * 4) * 8);
+  const int64_t recs = (int64_t)dssel::kAttendPartialWgs * dssel::kAttendHeadTile;
+  s.part_ml = off; off += align_up(recs * 2 * 4);
+  s.part_o = off;  off += align_up(recs * D * 4);
   s.total = off;
   return s;
 }
@@ -95,6 +103,38 @@ int check_args(const ds_sel_limits& lim, const ds_sel_args* a) {
     if (a->mask_row_stride != 0 && a->mask_row_stride < words) return DS_SEL_E_INVALID;
     if (a->mask_row_stride < 0 || a->mask_layer_stride < 0) return DS_SEL_E_INVALID;
     if (a->layers > 1 && a->mask_layer_stride < (a->rows - 1) * a->mask_row_stride + words)
+      return DS_SEL_E_INVALID;
+  }
+  return DS_SEL_OK;
+}
+
+int check_attend_args(const ds_sel_limits& lim, const ds_sel_attend_args* a) {
+  if (!a || a->struct_size != sizeof(ds_sel_attend_args) || a->reserved != 0) return DS_SEL_E_INVALID;
+  if (a->layers < 1 || a->rows < 1 || a->heads < 1 || a->dim < 1 || a->k < 1 || a->blocks < 0)
+    return DS_SEL_E_INVALID;
+  if (a->rows > DS_SEL_MAX_ROWS || a->k > DS_SEL_MAX_K || a->heads > DS_SEL_MAX_HEADS ||
+      a->blocks > DS_SEL_MAX_BLOCKS || !std::isfinite(a->scale))
+    return DS_SEL_E_INVALID;
+  if (a->dim != 32 && a->dim != 64 && a->dim != 128 && a->dim != 256) {
+    if (a->dim % 8 != 0 || a->dim > DS_SEL_MAX_DIM) return DS_SEL_E_INVALID;
+    return DS_SEL_E_UNSUPPORTED;
+  }
+  if (a->layers > lim.max_layers || a->rows > lim.max_rows || a->heads > lim.max_heads ||
+      a->dim > lim.max_dim || a->k > lim.max_k || a->blocks > lim.max_blocks)
+    return DS_SEL_E_CAPACITY;
+  if (!a->q || !a->idx || !a->out) return DS_SEL_E_INVALID;
+  if (!aligned(a->q, 16) || !aligned(a->idx, 4) || !aligned(a->count, 4) || !aligned(a->out, 4))
+    return DS_SEL_E_INVALID;
+  const int64_t N = a->blocks;
+  if (N > 0) {
+    if (!a->keys || !aligned(a->keys, 16) || !a->values || !aligned(a->values, 16))
+      return DS_SEL_E_INVALID;
+    if (a->ldk < a->dim || a->ldk % 8 != 0 || a->ldv < a->dim || a->ldv % 8 != 0)
+      return DS_SEL_E_INVALID;
+    if (a->key_layer_stride < 0 || a->key_layer_stride % 8 != 0 || a->value_layer_stride < 0 ||
+        a->value_layer_stride % 8 != 0)
+      return DS_SEL_E_INVALID;
+    if (a->layers > 1 && (a->key_layer_stride < N * a->ldk || a->value_layer_stride < N * a->ldv))
       return DS_SEL_E_INVALID;
   }
   return DS_SEL_OK;
@@ -179,6 +219,8 @@ int ds_sel_create(const ds_sel_limits* lim, ds_sel** out) {
   h->off_floor = s.floor;
   h->off_ccount = s.ccount;
   h->off_cand = s.cand;
+  h->off_part_ml = s.part_ml;
+  h->off_part_o = s.part_o;
   *out = h;
   return DS_SEL_OK;
 }
@@ -207,6 +249,60 @@ int ds_sel_score_select_profiled(ds_sel* h, const ds_sel_args* a, void* hip_stre
                                  void* const events[4]) {
   if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return DS_SEL_E_INVALID;
   return enqueue(h, a, hip_stream, events);
+}
+
+int ds_sel_check_attend_args(const ds_sel_limits* lim, const ds_sel_attend_args* a) {
+  const int rc = check_limits(lim);
+  if (rc != DS_SEL_OK) return rc;
+  return check_attend_args(*lim, a);
+}
+
+int ds_sel_attend(ds_sel* h, const ds_sel_attend_args* a, void* hip_stream) {
+  if (!h) return DS_SEL_E_INVALID;
+  const int rc = check_attend_args(h->lim, a);
+  if (rc != DS_SEL_OK) return rc;
+  dssel::AttendCall c{};
+  c.layers = a->layers;
+  c.rows = a->rows;
+  c.heads = a->heads;
+  c.dim = a->dim;
+  c.k = a->k;
+  c.blocks = a->blocks;
+  c.scale = a->scale;
+  c.head_tiles = (a->heads + dssel::kAttendHeadTile - 1) / dssel::kAttendHeadTile;
+  {
+    // Split each (layer, row, tile)'s selection only while the pairs alone
+    // leave compute units idle, and never past the scratch's record count.
+    const int64_t chunks = (a->k + dssel::kAttendChunk - 1) / dssel::kAttendChunk;
+    const int64_t base = (int64_t)a->layers * a->rows * c.head_tiles;
+    int64_t splits = 1;
+    if (base < h->compute_units) {
+      splits = h->compute_units / base;
+      const int64_t cap = dssel::kAttendPartialWgs / base;
+      if (splits > cap) splits = cap;
+      if (splits > chunks) splits = chunks;
+      if (splits < 1) splits = 1;
+    }
+    c.chunks_per_split = (int32_t)((chunks + splits - 1) / splits);
+    c.splits = (int32_t)((chunks + c.chunks_per_split - 1) / c.chunks_per_split);
+  }
+  c.q = static_cast<const uint16_t*>(a->q);
+  c.keys = static_cast<const uint16_t*>(a->keys);
+  c.ldk = a->ldk;
+  c.key_layer_stride = a->key_layer_stride;
+  c.values = static_cast<const uint16_t*>(a->values);
+  c.ldv = a->ldv;
+  c.value_layer_stride = a->value_layer_stride;
+  c.idx = a->idx;
+  c.count = a->count;
+  c.out = a->out;
+  char* base = static_cast<char*>(h->scratch);
+  c.part_ml = reinterpret_cast<float*>(base + h->off_part_ml);
+  c.part_o = reinterpret_cast<float*>(base + h->off_part_o);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  return with_device(h->lim.device, [&]() {
+    return dssel::launch_attend(c, stream) == hipSuccess ? (int)DS_SEL_OK : (int)DS_SEL_E_HIP;
+  });
 }
 
 }  // extern "C"

@@ -78,6 +78,37 @@ struct Call {
   uint64_t* cand;      // [L][R][cand_stride] (key << 32) | ~position, unordered
 };
 
+// Attention over the selected blocks.  One workgroup of kAttendThreads per
+// (head tile, split, row, layer); a split covers chunks_per_split chunks of
+// kAttendChunk selected blocks.  With several splits each writes a partial
+// record (max, sum, unnormalised o per head) that a second kernel merges.
+constexpr int kAttendThreads = 256;
+constexpr int kAttendHeadTile = 64;   // heads per workgroup, 16 per wave
+constexpr int kAttendChunk = 64;
+constexpr int kAttendMaxK = 2048;     // selections longer than this are not accepted
+constexpr int kAttendPartialWgs = 512;  // partial records the scratch holds (per head tile)
+
+struct AttendCall {
+  int32_t layers, rows, heads, dim, k;
+  int32_t head_tiles;        // ceil(heads / kAttendHeadTile)
+  int32_t splits;            // workgroups per (layer, row, head tile)
+  int32_t chunks_per_split;  // ceil(ceil(k / kAttendChunk) / splits)
+  int64_t blocks;
+  float scale;
+  const uint16_t* q;         // [L][R][heads][d]
+  const uint16_t* keys;
+  int64_t ldk, key_layer_stride;
+  const uint16_t* values;
+  int64_t ldv, value_layer_stride;
+  const int32_t* idx;        // [L][R][k]
+  const int32_t* count;      // [L][R] or null (all k slots)
+  float* out;                // [L][R][heads][d]
+  float* part_ml;            // [records][kAttendHeadTile][2] (max, sum), base-2 units
+  float* part_o;             // [records][kAttendHeadTile][d]
+};
+
+hipError_t launch_attend(const AttendCall& c, hipStream_t stream);
+
 hipError_t launch_prep(const Call& c, hipStream_t stream);
 hipError_t launch_score(const Call& c, hipStream_t stream);
 hipError_t launch_select(const Call& c, hipStream_t stream);

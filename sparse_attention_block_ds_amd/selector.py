@@ -25,7 +25,8 @@ DS_SEL_E_UNSUPPORTED = 6
 DS_SEL_FLAG_VALU_SCORE = 1
 
 EXPORTED = ("ds_sel_create", "ds_sel_score_select", "ds_sel_score_select_profiled",
-            "ds_sel_destroy", "ds_sel_check_args", "ds_sel_scratch_bytes", "ds_sel_status_string")
+            "ds_sel_destroy", "ds_sel_check_args", "ds_sel_scratch_bytes", "ds_sel_status_string",
+            "ds_sel_attend", "ds_sel_check_attend_args")
 
 
 class Limits(ctypes.Structure):
@@ -46,6 +47,17 @@ class Args(ctypes.Structure):
                 ("mask_layer_stride", ctypes.c_int64), ("limit", ctypes.c_void_p),
                 ("out_idx", ctypes.c_void_p), ("out_score", ctypes.c_void_p),
                 ("out_count", ctypes.c_void_p)]
+
+
+class AttendArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("layers", ctypes.c_int32),
+                ("rows", ctypes.c_int32), ("heads", ctypes.c_int32), ("dim", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("blocks", ctypes.c_int64), ("q", ctypes.c_void_p), ("keys", ctypes.c_void_p),
+                ("ldk", ctypes.c_int64), ("key_layer_stride", ctypes.c_int64),
+                ("values", ctypes.c_void_p), ("ldv", ctypes.c_int64),
+                ("value_layer_stride", ctypes.c_int64), ("idx", ctypes.c_void_p),
+                ("count", ctypes.c_void_p), ("out", ctypes.c_void_p)]
 
 
 class DsSelError(RuntimeError):
@@ -82,6 +94,10 @@ def load_library(path: Optional[str] = None):
     lib.ds_sel_check_args.restype = ctypes.c_int
     lib.ds_sel_scratch_bytes.argtypes = [P(Limits)]
     lib.ds_sel_scratch_bytes.restype = ctypes.c_int64
+    lib.ds_sel_attend.argtypes = [ctypes.c_void_p, P(AttendArgs), ctypes.c_void_p]
+    lib.ds_sel_attend.restype = ctypes.c_int
+    lib.ds_sel_check_attend_args.argtypes = [P(Limits), P(AttendArgs)]
+    lib.ds_sel_check_attend_args.restype = ctypes.c_int
     lib.ds_sel_status_string.argtypes = [ctypes.c_int]
     lib.ds_sel_status_string.restype = ctypes.c_char_p
     if default:
@@ -123,6 +139,23 @@ def make_args(q, w, keys, k, mask=None, limit=None, out_idx=None, out_score=None
         a.mask_layer_stride = mask.stride(0)
     a.limit = _ptr(limit)
     a.out_idx, a.out_score, a.out_count = _ptr(out_idx), _ptr(out_score), _ptr(out_count)
+    return a
+
+
+def make_attend_args(qa, keys, values, idx, count, scale, out):
+    """Fill an AttendArgs struct from tensors (no checks beyond shapes; the library validates)."""
+    L, R, H, d = qa.shape
+    N = keys.shape[1]
+    a = AttendArgs()
+    a.struct_size = ctypes.sizeof(AttendArgs)
+    a.layers, a.rows, a.heads, a.dim, a.k, a.blocks = L, R, H, d, idx.shape[2], N
+    a.scale, a.reserved = float(scale), 0
+    a.q = _ptr(qa)
+    a.keys = _ptr(keys) if N > 0 else None
+    a.ldk, a.key_layer_stride = keys.stride(1), keys.stride(0)
+    a.values = _ptr(values) if N > 0 else None
+    a.ldv, a.value_layer_stride = values.stride(1), values.stride(0)
+    a.idx, a.count, a.out = _ptr(idx), _ptr(count), _ptr(out)
     return a
 
 
@@ -187,6 +220,28 @@ class Selector:
                                                        ctypes.c_void_p(handle), ev)
         if rc != DS_SEL_OK:
             raise DsSelError(rc, "ds_sel_score_select")
+        return out
+
+
+    def attend(self, qa, keys, values, idx, count=None, scale=None, out=None, stream=None):
+        """Enqueue attention over a selection; returns out f32 [L,R,Ha,d].
+
+        qa bf16 [L,R,Ha,d]; keys, values bf16 [L,N,ld] (unit stride in the last
+        dim); idx int32 [L,R,k] and count int32 [L,R] or None, as score_select
+        returns them; scale defaults to 1/sqrt(d).  Asynchronous on `stream`.
+        """
+        torch = self._torch
+        if scale is None:
+            scale = 1.0 / float(qa.shape[3]) ** 0.5
+        if out is None:
+            out = torch.empty(tuple(qa.shape), dtype=torch.float32, device=qa.device)
+        a = make_attend_args(qa, keys, values, idx, count, scale, out)
+        if stream is None:
+            stream = torch.cuda.current_stream(qa.device)
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        rc = self.lib.ds_sel_attend(self.handle, ctypes.byref(a), ctypes.c_void_p(handle))
+        if rc != DS_SEL_OK:
+            raise DsSelError(rc, "ds_sel_attend")
         return out
 
 

@@ -237,3 +237,39 @@ def make_custom(layers, rows, heads, dim, blocks, k, *, seed, values="normal", l
     if limits is not None:
         lim = np.broadcast_to(np.asarray(limits, np.int32), (L, R)).copy()
     return Problem(name, k, q, w, keys, mask, lim, integer, {"seed": seed})
+
+
+# ------------------------------------------------------------ attention over a selection
+#
+# The attention step reads, besides the selection and the block keys K, a
+# query per attention head and a value row per block.  The pages give neither;
+# this library's recipe: Ha = 64 attention heads of dimension d, the
+# attention queries qa ~ N(0,1) and the values V ~ N(0,1), drawn in that order
+# from default_rng(seed + 100) and rounded to bf16 (nearest, ties to even).
+
+def attend_inputs(layers, rows, heads, dim, blocks, *, seed, ldv=None):
+    """(qa [L][R][Ha][d], values [L][N][ldv]) as bf16 bits; columns past d hold NaN bits."""
+    rng = np.random.default_rng(seed + 100)
+    ldv = dim if ldv is None else ldv
+    qa = _normal_bits(rng, (layers, rows, heads, dim))
+    values = _normal_bits(rng, (layers, blocks, ldv))
+    if ldv > dim:
+        values[:, :, dim:] = 0x7FC0
+    return qa, values
+
+
+def random_selection(layers, rows, blocks, k, *, seed, count=None):
+    """A selection in the layout the selection returns: idx [L][R][k] int32 of
+    distinct blocks in random order, -1 past count, and count [L][R] int32.
+    count: None (min(k, N) everywhere), an int, or an int array [L][R]."""
+    rng = np.random.default_rng(seed + 200)
+    if count is None:
+        count = min(k, blocks)
+    cnt = np.broadcast_to(np.asarray(count, np.int32), (layers, rows)).copy()
+    idx = np.full((layers, rows, k), -1, np.int32)
+    for l in range(layers):
+        for r in range(rows):
+            c = int(cnt[l, r])
+            if c > 0:
+                idx[l, r, :c] = rng.choice(blocks, size=c, replace=False)
+    return idx, cnt

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("ds_sel_create", "ds_sel_score_select", "ds_sel_destroy"):
+    for required in ("ds_sel_create", "ds_sel_score_select", "ds_sel_destroy", "ds_sel_attend"):
         assert required in names
     assert set(names) == set(sel.EXPORTED)
 
@@ -51,9 +51,13 @@ def test_struct_layout_matches_header(tmp_path):
 #define F(T, m) printf(#T "." #m " %zu\n", offsetof(T, m))
 int main(void) {
   printf("ds_sel_limits %zu\nds_sel_args %zu\n", sizeof(ds_sel_limits), sizeof(ds_sel_args));
+  printf("ds_sel_attend_args %zu\n", sizeof(ds_sel_attend_args));
   F(ds_sel_limits, max_blocks); F(ds_sel_args, blocks); F(ds_sel_args, q); F(ds_sel_args, ldk);
   F(ds_sel_args, mask); F(ds_sel_args, mask_layer_stride); F(ds_sel_args, limit);
   F(ds_sel_args, out_count);
+  F(ds_sel_attend_args, scale); F(ds_sel_attend_args, blocks); F(ds_sel_attend_args, keys);
+  F(ds_sel_attend_args, values); F(ds_sel_attend_args, value_layer_stride);
+  F(ds_sel_attend_args, idx); F(ds_sel_attend_args, out);
   return 0;
 }
 """)
@@ -64,10 +68,13 @@ int main(void) {
                                                    check=True).stdout.splitlines())
     assert int(lines["ds_sel_limits"]) == ctypes.sizeof(sel.Limits)
     assert int(lines["ds_sel_args"]) == ctypes.sizeof(sel.Args)
+    assert int(lines["ds_sel_attend_args"]) == ctypes.sizeof(sel.AttendArgs)
+    classes = {"ds_sel_limits": sel.Limits, "ds_sel_args": sel.Args,
+               "ds_sel_attend_args": sel.AttendArgs}
     for key, value in lines.items():
         if "." in key:
             struct, field = key.split(".")
-            cls = sel.Limits if struct == "ds_sel_limits" else sel.Args
+            cls = classes[struct]
             assert getattr(cls, field).offset == int(value), key
 
 
@@ -179,7 +186,8 @@ def test_scratch_bytes(lib):
     up = lambda v: (v + 255) // 256 * 256
     L, R, D, N = 43, 6, 128, 75000
     expect = (up(L * R * D * 4) + up(3 * L * R * D * 2) + up(L * N * 4) + up(9 * L * 4)
-              + up(L * R * 4) + up(L * R * 32 * 4) + up(L * R * ((N + 3) // 4 * 4) * 8))
+              + up(L * R * 4) + up(L * R * 32 * 4) + up(L * R * ((N + 3) // 4 * 4) * 8)
+              + up(512 * 64 * 2 * 4) + up(512 * 64 * D * 4))
     assert nbytes == expect
 
 
@@ -199,3 +207,68 @@ def test_destroy_null_is_noop_and_status_strings(lib):
     assert lib.ds_sel_status_string(0) == b"ok"
     assert lib.ds_sel_status_string(sel.DS_SEL_E_CAPACITY) == b"exceeds the handle's capacity"
     assert lib.ds_sel_status_string(99) == b"unknown status"
+
+
+# ------------------------------------------------------------ attention over a selection
+def _attend_args(L=2, R=6, H=64, d=128, N=75000, k=512, with_count=True, ldk=None, ldv=None):
+    ldk, ldv = ldk or d, ldv or d
+    qa = FakeTensor((L, R, H, d), ptr=0x1000)
+    keys = FakeTensor((L, N, ldk), (N * ldk, ldk, 1), ptr=0x20000)
+    values = FakeTensor((L, N, ldv), (N * ldv, ldv, 1), ptr=0x90000)
+    idx = FakeTensor((L, R, k), ptr=0x60000)
+    count = FakeTensor((L, R), ptr=0x80000) if with_count else None
+    out = FakeTensor((L, R, H, d), ptr=0xA0000)
+    return sel.make_attend_args(qa, keys, values, idx, count, 1.0 / d ** 0.5, out)
+
+
+def check_attend(lib, args, **lim):
+    limits = sel.make_limits(**{**LIM, **lim})
+    return lib.ds_sel_check_attend_args(ctypes.byref(limits), ctypes.byref(args))
+
+
+def test_attend_valid_arguments_pass(lib):
+    assert check_attend(lib, _attend_args()) == sel.DS_SEL_OK
+    assert check_attend(lib, _attend_args(with_count=False)) == sel.DS_SEL_OK
+    assert check_attend(lib, _attend_args(d=64, H=20, ldk=72, ldv=80)) == sel.DS_SEL_OK
+    a = _attend_args(N=0)
+    a.keys = a.values = None
+    assert check_attend(lib, a) == sel.DS_SEL_OK
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("layers", 0, sel.DS_SEL_E_INVALID),
+    ("rows", 9, sel.DS_SEL_E_INVALID),
+    ("heads", 0, sel.DS_SEL_E_INVALID),
+    ("k", 0, sel.DS_SEL_E_INVALID),
+    ("k", 4096, sel.DS_SEL_E_INVALID),
+    ("dim", 96, sel.DS_SEL_E_UNSUPPORTED),
+    ("dim", 100, sel.DS_SEL_E_INVALID),
+    ("scale", float("inf"), sel.DS_SEL_E_INVALID),
+    ("scale", float("nan"), sel.DS_SEL_E_INVALID),
+    ("reserved", 1, sel.DS_SEL_E_INVALID),
+    ("q", None, sel.DS_SEL_E_INVALID),
+    ("q", 0x1008, sel.DS_SEL_E_INVALID),            # not 16-byte aligned
+    ("idx", None, sel.DS_SEL_E_INVALID),
+    ("idx", 0x60002, sel.DS_SEL_E_INVALID),
+    ("count", 0x80001, sel.DS_SEL_E_INVALID),
+    ("out", None, sel.DS_SEL_E_INVALID),
+    ("values", None, sel.DS_SEL_E_INVALID),
+    ("values", 0x90008, sel.DS_SEL_E_INVALID),
+    ("ldv", 120, sel.DS_SEL_E_INVALID),
+    ("ldv", 132, sel.DS_SEL_E_INVALID),
+    ("value_layer_stride", 8, sel.DS_SEL_E_INVALID),  # layers overlap
+    ("key_layer_stride", 4, sel.DS_SEL_E_INVALID),
+    ("struct_size", 8, sel.DS_SEL_E_INVALID),
+])
+def test_attend_bad_arguments_rejected(lib, field, value, expect):
+    a = _attend_args()
+    setattr(a, field, value)
+    assert check_attend(lib, a) == expect
+
+
+@pytest.mark.parametrize("field,value", [("layers", 44), ("rows", 7), ("heads", 65), ("k", 513),
+                                         ("blocks", 75001)])
+def test_attend_capacity_enforced(lib, field, value):
+    a = _attend_args(L=1)
+    setattr(a, field, value)
+    assert check_attend(lib, a) == sel.DS_SEL_E_CAPACITY
