@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--engine", default="mfma", choices=["mfma", "valu"],
                     help="key-stream engine: bf16 matrix cores (default) or fp32 vector FMAs")
+    ap.add_argument("--no-attend", action="store_true",
+                    help="skip the attention-over-the-selection leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB read + 1 GiB write elementwise kernel, to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters")
@@ -170,6 +172,58 @@ def cpu_baseline(p, gpu_out, budget_s):
     }
 
 
+def attend_leg(p, selector, keys, idx, count, steps, warmup, stream):
+    """Attention over the chain's selection (64 query heads per row, bf16 q and
+    values drawn on the device from a fixed seed), timed with HIP events on the
+    launch stream; two (layer, row) pairs are checked against the fp64 oracle.
+
+    Algorithmic bytes per (layer, row): count x 2 x 2d (the selected K and V
+    rows) + H d 2 (q) + H d 4 (the fp32 output); flops: 4 H d per selected block."""
+    import numpy as np
+    import torch
+    import oracle
+
+    L, R, H, d, N = p.layers, p.rows, p.heads, p.dim, p.blocks
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(1234)
+    qa = torch.randn((L, R, H, d), generator=g, device="cuda:0").to(torch.bfloat16)
+    values = torch.randn((L, N, d), generator=g, device="cuda:0").to(torch.bfloat16)
+    out = torch.empty((L, R, H, d), dtype=torch.float32, device="cuda:0")
+    for _ in range(warmup):
+        selector.attend(qa, keys, values, idx, count, out=out, stream=stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        selector.attend(qa, keys, values, idx, count, out=out, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    cnt = count.cpu().numpy().astype(np.int64)
+    sel_blocks = int(np.clip(cnt, 0, p.k).sum())
+    nbytes = sel_blocks * 2 * 2 * d + L * R * H * d * (2 + 4)
+    flops = 4.0 * H * d * sel_blocks
+    # parity sample: first and last (layer, row)
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    worst = 0.0
+    for l, r in ((0, 0), (L - 1, R - 1)):
+        ref = oracle.attend(bits(qa[l:l + 1, r:r + 1]), bits(keys[l:l + 1]), bits(values[l:l + 1]),
+                            idx[l:l + 1, r:r + 1].cpu().numpy(), count[l:l + 1, r:r + 1].cpu().numpy(),
+                            1.0 / np.sqrt(d))
+        err = np.abs(out[l:l + 1, r:r + 1].cpu().numpy() - ref).max() / max(np.abs(ref).max(), 1e-30)
+        worst = max(worst, float(err))
+    if not worst <= 1e-4:
+        log(f"[bench] ATTENTION PARITY FAILURE: relative max error {worst:.3e}")
+        sys.exit(3)
+    return {"kernel": "attend (softmax(q K^T) V over the selected blocks)", "ms": ms,
+            "selected_blocks": sel_blocks, "algorithmic_bytes": nbytes,
+            "achieved_gbs": nbytes / (ms / 1000.0) / 1e9,
+            "frac_hbm": nbytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
+            "tflops": flops / (ms / 1000.0) / 1e12,
+            "parity": f"2 (layer,row) pairs vs the fp64 oracle, max relative error {worst:.1e}"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -260,6 +314,12 @@ def main():
     else:
         parity = "not checked (--no-cpu-baseline)"
 
+    attend = None
+    if not args.no_attend and p.heads >= 16:
+        last = outs[(args.steps - 1) % n_sets]
+        attend = attend_leg(p, selector, sets[(args.steps - 1) % n_sets][2], last[0], last[2],
+                            min(args.steps, 20), 3, stream)
+
     traffic = load_traffic(p.name)
     line = {
         "metric": "candidate blocks selected/sec per layer-row; achieved HBM GB/s vs peak",
@@ -298,6 +358,7 @@ def main():
         "layer_row_selections_per_s": p.layers * p.rows / (ms_per_step / 1000.0),
         "chain_algorithmic_gbs": alg["total"] / (ms_per_step / 1000.0) / 1e9,
         "parity": parity,
+        "attend": attend,
     }
     print(json.dumps(line), flush=True)
     selector.close()

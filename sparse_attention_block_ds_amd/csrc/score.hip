@@ -27,11 +27,16 @@
 //       VALU engine: d/8 lanes per key row, 8 fp32 FMAs per lane and row, a
 //       butterfly across the row's lanes.
 //  3. Epilogue: the score becomes an order-preserving radix key; keys at or
-//     above the row's floor are staged per wave and row in LDS and flushed to
-//     the row's candidate list with one global atomic per flush.  Nothing is
-//     written for the other keys: writing every key would add one write for
-//     every 10 to 64 bytes read, and writes mixed into the read stream cost
-//     the stream far more than their size.
+//     above the row's floor are staged in one LDS list per wave, tagged with
+//     their row (one ballot per row set of the MFMA output, so a group costs
+//     two ballots whatever the row count).  At the end of the piece the
+//     workgroup counts its staged keys per row, reserves room in each row's
+//     candidate list with one global atomic per row, and copies them out; a
+//     wave whose list fills mid-piece distributes it the same way with
+//     atomics of its own.  Nothing is written for the keys below the floor:
+//     writing every key would add one write for every 10 to 64 bytes read,
+//     and writes mixed into the read stream cost the stream far more than
+//     their size.
 #include "device_util.h"
 #include "dssel_internal.h"
 
@@ -51,34 +56,26 @@ __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-__device__ __forceinline__ uint64_t pack_candidate(uint32_t key, int pos) {
-  return ((uint64_t)key << 32) | (uint32_t)~(uint32_t)pos;
-}
+// A staged candidate: its key and its layer position, tagged with its row.
+constexpr int kRowShift = 26;  // positions are below 2^26 (DS_SEL_MAX_BLOCKS)
+static_assert(kMaxRows <= 32, "row tag must fit above the position bits");
 
 template <int R>
 struct ScoreShared {
   int32_t list[kPiece];
-  uint64_t stage[kWaves][R][kWaveCandBuf];
+  uint2 stage[kWaves][kWaveStage];  // (key, position | row << kRowShift)
   int P[kMaxRows];
   int64_t lim[kMaxRows];
   uint32_t floor[kMaxRows];
   int piece[4];
-  int wstaged[kWaves][kMaxRows];  // end of piece: each wave's staged count per row
-  int base[kMaxRows];             // end of piece: the workgroup's slot in each row's list
+  int rowcnt[kWaves][kMaxRows];  // end of piece: each wave's staged count per row
+  int base[kMaxRows];            // end of piece: the workgroup's slot in each row's list
 };
 
-// A wave's n staged candidates of one row go to the row's list, at a slot
-// taken with one atomic.  It runs once per kWaveCandBuf candidates of a wave
-// and row: a cold path, laid out away from the stream loop.
-__device__ __forceinline__ void flush_staged(const uint64_t* stage, int n, int32_t* counter,
-                                                       uint64_t* list, int64_t stride) {
-  int base = 0;
-  if (lane_id() == 0) base = atomicAdd(counter, n);
-  base = __shfl(base, 0, kWave);
-  wave_lds_sync();
-  for (int i = lane_id(); i < n; i += kWave)
-    if (base + i < stride) list[base + i] = stage[i];
-  wave_lds_sync();
+// Number of lanes below this one whose bit is set in `bal`.
+__device__ __forceinline__ int lanes_below(uint64_t bal) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
 // Per-wave candidate staging and the piece's context.
@@ -88,8 +85,8 @@ struct PieceCtx {
   int pj, pn, nl;              // interleaved: piece j of pn, layer's admitted count nl
   int mode;
   const ScoreShared<R>* sh;
-  uint64_t* stage;             // this wave's [R][kWaveCandBuf]
-  int staged[R];               // per row, the same in every lane of the wave
+  uint2* stage;                // this wave's [kWaveStage]
+  int nst;                     // staged entries, the same in every lane of the wave
   int32_t* cand_count;         // [R][kCountPad] of this layer
   uint64_t* cand;              // [R][stride] of this layer
   int64_t stride;
@@ -108,39 +105,78 @@ struct PieceCtx {
     return mode == kNoMask ? pos_of(e) : sh->list[e];
   }
 
-  // Is position pos_of(e) a candidate of row r with score s?  Sets its key.
-  __device__ __forceinline__ bool want(int r, int e, float s, uint32_t* key) const {
-    const int pos = pos_of(e);
-    if (e >= cnt || pos >= sh->P[r]) return false;
-    if (mode == kRowMask) {  // the union list also holds blocks other rows admit
-      const int b = sh->list[e];
-      const uint32_t word = mask_l[r * mask_row_stride + (b >> 5)];
-      if (!((word >> (b & 31)) & 1u) || (int64_t)b >= sh->lim[r]) return false;
-    }
-    *key = score_to_key(s);
-    return *key >= sh->floor[r];
+  // With a mask row per query row, the union list also holds blocks that row
+  // r does not admit: test its own bit and limit.
+  __device__ __forceinline__ bool row_admits(int r, int e) const {
+    const int b = sh->list[e];
+    const uint32_t word = mask_l[r * mask_row_stride + (b >> 5)];
+    return ((word >> (b & 31)) & 1u) && (int64_t)b < sh->lim[r];
   }
 
-  // Copy row r's staged candidates to its global list (whole wave).  Only
-  // taken when a wave's staging for a row fills up.
-  __device__ __forceinline__ void flush(int r) {
-    flush_staged(stage + r * kWaveCandBuf, staged[r], cand_count + r * kCountPad, cand + r * stride,
-                 stride);
-    staged[r] = 0;
-  }
-
-  // Append the lanes' candidates of row r; called by every lane of the wave.
-  __device__ __forceinline__ void append(int r, bool ok, uint32_t key, int e) {
+  // Stage the lanes' candidates: lane i offers (key, position pos of row r)
+  // when ok.  Called by every lane of the wave.
+  __device__ __forceinline__ void append(bool ok, uint32_t key, int pos, int r) {
     const uint64_t bal = __ballot(ok);
     if (bal == 0) return;
     const int n = __popcll(bal);
-    if (__builtin_expect(staged[r] + n > kWaveCandBuf, 0)) flush(r);
-    if (ok) {
-      const int lane = lane_id();
-      const uint64_t below = lane == 0 ? 0ull : (bal & (~0ull >> (kWave - lane)));
-      stage[r * kWaveCandBuf + staged[r] + __popcll(below)] = pack_candidate(key, pos_of(e));
+    if (__builtin_expect(nst + n > kWaveStage, 0)) spill();
+    if (ok) stage[nst + lanes_below(bal)] = make_uint2(key, (uint32_t)pos | ((uint32_t)r << kRowShift));
+    nst += n;
+  }
+
+  // Lane r (< R) gets the number of staged entries of row r.
+  __device__ int count_rows() const {
+    const int lane = lane_id();
+    int mine = 0;
+    for (int i0 = 0; i0 < nst; i0 += kWave) {
+      const int i = i0 + lane;
+      const int row = i < nst ? (int)(stage[i].y >> kRowShift) : -1;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int n = __popcll(__ballot(row == r));
+        if (lane == r) mine += n;
+      }
     }
-    staged[r] += n;
+    return mine;
+  }
+
+  // Copy the staged entries out; lane r (< R) holds the first slot of row r's
+  // run in the row's list.  Entries keep their staging order within a row.
+  __device__ void write_out(int start) const {
+    const int lane = lane_id();
+    int run = start;  // lane r: next free slot of row r
+    for (int i0 = 0; i0 < nst; i0 += kWave) {
+      const int i = i0 + lane;
+      const uint2 v = i < nst ? stage[i] : make_uint2(0u, 0xFFFFFFFFu);
+      const int row = i < nst ? (int)(v.y >> kRowShift) : -1;
+      uint64_t my = 0;
+      int add = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint64_t b = __ballot(row == r);
+        if (row == r) my = b;
+        if (lane == r) add = __popcll(b);
+      }
+      const int slot = __shfl(run, row < 0 ? 0 : row, kWave) + lanes_below(my);
+      if (row >= 0 && slot < stride) {
+        const uint32_t pos = v.y & ((1u << kRowShift) - 1u);
+        cand[row * stride + slot] = ((uint64_t)v.x << 32) | (uint32_t)~pos;
+      }
+      run += add;
+    }
+  }
+
+  // Mid-piece: the wave's list is full.  Distribute it with one atomic per
+  // row of the wave's own (a cold path).
+  __device__ void spill() {
+    wave_lds_sync();
+    const int lane = lane_id();
+    const int n = count_rows();
+    int start = 0;
+    if (lane < R && n > 0) start = atomicAdd(&cand_count[lane * kCountPad], n);
+    write_out(start);
+    wave_lds_sync();
+    nst = 0;
   }
 };
 
@@ -201,14 +237,28 @@ struct MfmaEngine {
     }
     const int lane = lane_id();
     const int e = g0 + (lane & 15), g = lane >> 4;
+    const int pos = t.pos_of(e);
+    const bool live = e < t.cnt;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      uint32_t key = 0;
-      const int r = 4 * s + g;
-      const bool ok = r < R && t.want(r, e, (acc[s][0] + acc[s][1]) + acc[s][2], &key);
+      const uint32_t key = score_to_key((acc[s][0] + acc[s][1]) + acc[s][2]);
+      bool ok = live && pos < lp[s] && key >= lf[s];
+      if (t.mode == kRowMask && ok) ok = t.row_admits(4 * s + g, e);
+      t.append(ok, key, pos, 4 * s + g);
+    }
+  }
+
+  // The lane's rows of the MFMA output (row 4 s + lane / 16 of set s): their
+  // admitted counts (0 past R) and floors.
+  int lp[S];
+  uint32_t lf[S];
+  __device__ void bind_rows(const ScoreShared<R>& sh) {
+    const int g = lane_id() >> 4;
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
-        if (4 * s + gg < R) t.append(4 * s + gg, ok && g == gg, key, e);
+    for (int s = 0; s < S; ++s) {
+      const int r = 4 * s + g;
+      lp[s] = r < R ? sh.P[r] : 0;
+      lf[s] = r < R ? sh.floor[r] : 0u;
     }
   }
 };
@@ -269,14 +319,19 @@ struct ValuEngine {
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] += __shfl_xor(acc[r], m, kWave);
       const int e = g0 + u * RPI + rr;
+      const int pos = t.pos_of(e);
+      const bool live = e < t.cnt;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        uint32_t key = 0;
-        const bool ok = r % LPR == slice && t.want(r, e, acc[r], &key);
-        t.append(r, ok, key, e);
+        const uint32_t key = score_to_key(acc[r]);
+        bool ok = r % LPR == slice && live && pos < t.sh->P[r] && key >= t.sh->floor[r];
+        if (t.mode == kRowMask && ok) ok = t.row_admits(r, e);
+        t.append(ok, key, pos, r);
       }
     }
   }
+
+  __device__ void bind_rows(const ScoreShared<R>&) {}
 };
 
 // Runs the wave's groups g0, g0 + step, ... < cnt through a ring of NBUF load
@@ -410,9 +465,9 @@ __device__ __forceinline__ void score_body(const Call& c) {
 
   pc.mode = c.mode;
   pc.sh = &sh;
-  pc.stage = &sh.stage[wave][0][0];
-#pragma unroll
-  for (int r = 0; r < R; ++r) pc.staged[r] = 0;
+  pc.stage = &sh.stage[wave][0];
+  pc.nst = 0;
+  eng.bind_rows(sh);
   pc.cand_count = c.cand_count + (int64_t)sl * R * kCountPad;
   pc.cand = c.cand + (int64_t)sl * R * c.cand_stride;
   pc.stride = c.cand_stride;
@@ -422,26 +477,22 @@ __device__ __forceinline__ void score_body(const Call& c) {
                                  wave * kGroup, kWaves * kGroup);
   // End of the piece: one counter update per row for the whole workgroup.
   const int lane = lane_id();
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) sh.wstaged[wave][r] = pc.staged[r];
-  }
+  const int mine = pc.count_rows();  // lane r: this wave's staged entries of row r
+  if (lane < R) sh.rowcnt[wave][lane] = mine;
   __syncthreads();
   if (tid < R) {
     int n = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) n += sh.wstaged[w][tid];
+    for (int w = 0; w < kWaves; ++w) n += sh.rowcnt[w][tid];
     sh.base[tid] = n ? atomicAdd(&pc.cand_count[tid * kCountPad], n) : 0;
   }
   __syncthreads();
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    int off = sh.base[r];
-    for (int w = 0; w < wave; ++w) off += sh.wstaged[w][r];
-    const uint64_t* st = pc.stage + r * kWaveCandBuf;
-    for (int i = lane; i < pc.staged[r]; i += kWave)
-      if (off + i < pc.stride) pc.cand[r * pc.stride + off + i] = st[i];
+  int start = 0;
+  if (lane < R) {
+    start = sh.base[lane];
+    for (int w = 0; w < wave; ++w) start += sh.rowcnt[w][lane];
   }
+  pc.write_out(start);
 }
 
 // The MFMA kernel is held to 128 registers (four waves per SIMD, 16 per
