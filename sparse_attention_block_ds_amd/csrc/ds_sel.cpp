@@ -339,7 +339,7 @@ int enqueue(ds_sel* h, const ds_sel_args* a, void* hip_stream, void* const* even
     // Score grid: every resident slot (four workgroups per compute unit), and
     // enough workgroups that a piece never exceeds kScorePieceMax positions
     // even when every block is admitted.
-    const int64_t slots = (int64_t)dssel::kScoreRounds * dssel::kScoreWgsPerCu * h->compute_units;
+    const int64_t slots = (int64_t)dssel::kScoreWgsPerCu * h->compute_units;
     const int64_t need = a->layers + ((int64_t)a->layers * a->blocks + dssel::kScorePieceMax - 1) /
                                          dssel::kScorePieceMax;
     c.score_slots = (int32_t)slots;

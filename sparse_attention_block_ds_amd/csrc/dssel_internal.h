@@ -32,10 +32,6 @@ constexpr int kScoreThreads = 256;           // 4 waves
 constexpr int kScorePieceMax = 2048;         // admitted positions per score workgroup: at most,
 constexpr int kScorePieceMin = 64;           // and at least
 constexpr int kScoreWgsPerCu = 4;            // resident score workgroups per compute unit
-#ifndef DSSEL_SCORE_ROUNDS
-#define DSSEL_SCORE_ROUNDS 1
-#endif
-constexpr int kScoreRounds = DSSEL_SCORE_ROUNDS;  // pieces per resident slot (dispatcher-balanced rounds)
 constexpr int kWaveStage = 512;              // per-wave candidate staging, all rows (LDS)
 constexpr int kCountPad = 32;                // candidate counters sit 128 bytes apart
 

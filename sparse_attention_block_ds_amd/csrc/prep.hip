@@ -439,8 +439,11 @@ __device__ void expand_tiles(const Call& c, int l, int x, ExpandShared& sh) {
 template <int R, int D>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(Call c) {
   __shared__ PrepShared sh;
-  if (blockIdx.x == 0) fold_count_floor<R, D>(c, blockIdx.y, sh.f);
-  else expand_tiles<R>(c, blockIdx.y, blockIdx.x, sh.e);
+  // blockIdx.x is the layer, so that consecutive workgroups (which the
+  // dispatcher deals out to the XCDs in turn) belong to different layers and
+  // the layers' fold workgroups spread over every XCD.
+  if (blockIdx.y == 0) fold_count_floor<R, D>(c, blockIdx.x, sh.f);
+  else expand_tiles<R>(c, blockIdx.x, blockIdx.y, sh.e);
 }
 
 template <int R>
@@ -459,7 +462,7 @@ hipError_t launch_r(const Call& c, dim3 grid, hipStream_t stream) {
 
 hipError_t launch_prep(const Call& c, hipStream_t stream) {
   const int expanders = c.mode == kNoMask ? 0 : (c.ntiles + kPrepTilesPerWg - 1) / kPrepTilesPerWg;
-  dim3 grid(1 + expanders, c.layers);
+  dim3 grid(c.layers, 1 + expanders);
   switch (c.rows) {
     case 1: return launch_r<1>(c, grid, stream);
     case 2: return launch_r<2>(c, grid, stream);

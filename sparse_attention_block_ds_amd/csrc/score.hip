@@ -447,10 +447,20 @@ __device__ __forceinline__ void score_body(const Call& c) {
     pc.cnt = (pc.off + pz.T < nl ? pc.off + pz.T : nl) - pc.off;
   }
   if (c.mode != kNoMask) {
+    // the piece's slice of the index: every load issued before any is stored
     const int32_t* list = c.list + (int64_t)sl * N;
-    for (int i = tid; i < pc.cnt; i += kScoreThreads) {
+    constexpr int kPer = (kPiece + kScoreThreads - 1) / kScoreThreads;
+    int32_t v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kScoreThreads;
       const int pos = pc.pos_of(i);
-      sh.list[i] = pos < nl ? list[pos] : 0;
+      v[u] = (i < pc.cnt && pos < nl) ? list[pos] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kScoreThreads;
+      if (i < pc.cnt) sh.list[i] = v[u];
     }
   }
   if (tid < kMaxRows) {
