@@ -296,30 +296,66 @@ __global__ __launch_bounds__(kThreads) void attend_partial_kernel(AttendCall c) 
 }
 
 // Merge the splits of each head: with M = max_s m_s,
-//   o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+//   o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+// summed in ascending split order.  64 threads per head (dims t, t + 64, ...),
+// four heads per workgroup; the split records are read in batches whose loads
+// do not wait on each other.
+constexpr int kCombineHeads = kThreads / kWave;  // heads per combine workgroup
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void attend_combine_kernel(AttendCall c) {
-  const int tile = blockIdx.x, r = blockIdx.y, l = blockIdx.z;
+  constexpr int kPer = (D + kWave - 1) / kWave;  // dims per thread
+  constexpr int kB = 4;                          // split records per batch
+  const int tile = blockIdx.x / (kAttendHeadTile / kCombineHeads);
+  const int hl = (blockIdx.x % (kAttendHeadTile / kCombineHeads)) * kCombineHeads + threadIdx.x / kWave;
+  const int h = tile * kAttendHeadTile + hl;
+  if (h >= c.heads) return;  // a whole wave (no barriers below)
+  const int t = threadIdx.x % kWave;
+  const int r = blockIdx.y, l = blockIdx.z;
   const int64_t lr = (int64_t)l * c.rows + r;
-  const int64_t rec0 = (lr * c.head_tiles + tile) * c.splits * kAttendHeadTile;
-  for (int x = threadIdx.x; x < kAttendHeadTile * D; x += kThreads) {
-    const int hl = x / D, i = x % D;
-    const int h = tile * kAttendHeadTile + hl;
-    if (h >= c.heads) break;  // x only grows
-    float mx = -__builtin_inff();
-    for (int s = 0; s < c.splits; ++s) mx = fmaxf(mx, c.part_ml[2 * (rec0 + s * kAttendHeadTile + hl)]);
-    float z = 0.0f, acc = 0.0f;
-    if (mx != -__builtin_inff()) {
-      for (int s = 0; s < c.splits; ++s) {
-        const int64_t rec = rec0 + s * kAttendHeadTile + hl;
-        const float ms = c.part_ml[2 * rec];
-        if (ms == -__builtin_inff()) continue;
-        const float f = exp2f(ms - mx);
-        z += f * c.part_ml[2 * rec + 1];
-        acc += f * c.part_o[rec * D + i];
+  const int64_t rec0 = (lr * c.head_tiles + tile) * c.splits * kAttendHeadTile + hl;  // split s: + s * 64
+  float mx = -__builtin_inff();
+  for (int s0 = 0; s0 < c.splits; s0 += kB) {
+    float mv[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      mv[b] = s0 + b < c.splits ? c.part_ml[2 * (rec0 + (int64_t)(s0 + b) * kAttendHeadTile)] : -__builtin_inff();
+#pragma unroll
+    for (int b = 0; b < kB; ++b) mx = fmaxf(mx, mv[b]);
+  }
+  float z = 0.0f, acc[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) acc[i] = 0.0f;
+  if (mx != -__builtin_inff()) {
+    for (int s0 = 0; s0 < c.splits; s0 += kB) {
+      float ms[kB], ls[kB], ov[kB][kPer];
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const bool ok = s0 + b < c.splits;
+        const int64_t rec = rec0 + (int64_t)(s0 + b) * kAttendHeadTile;
+        ms[b] = ok ? c.part_ml[2 * rec] : -__builtin_inff();
+        ls[b] = ok ? c.part_ml[2 * rec + 1] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int dim = t + kWave * i;
+          ov[b][i] = (ok && dim < D) ? c.part_o[rec * D + dim] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        if (ms[b] == -__builtin_inff()) continue;
+        const float f = exp2f(ms[b] - mx);
+        z += f * ls[b];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) acc[i] += f * ov[b][i];
       }
     }
-    c.out[(lr * c.heads + h) * D + i] = z > 0.0f ? acc / z : 0.0f;
+  }
+  float* oh = c.out + (lr * c.heads + h) * D;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int dim = t + kWave * i;
+    if (dim < D) oh[dim] = z > 0.0f ? acc[i] / z : 0.0f;
   }
 }
 
@@ -330,8 +366,9 @@ hipError_t launch_attend_d(const AttendCall& c, hipStream_t stream) {
   if (c.splits > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attend_combine_kernel<D>, dim3(c.head_tiles, c.rows, c.layers), dim3(kThreads), 0,
-                       stream, c);
+    hipLaunchKernelGGL(attend_combine_kernel<D>,
+                       dim3(c.head_tiles * (kAttendHeadTile / kCombineHeads), c.rows, c.layers), dim3(kThreads),
+                       0, stream, c);
   }
   return hipGetLastError();
 }
