@@ -23,6 +23,8 @@ struct ds_sel {
 static_assert(DS_SEL_MAX_K <= 2048, "select kernel LDS sized for k <= 2048");
 static_assert(DS_SEL_MAX_K <= dssel::kAttendMaxK, "attention kernel LDS sized for k <= kAttendMaxK");
 static_assert(DS_SEL_MAX_DIM <= 256, "attention kernels built for d <= 256");
+static_assert(DS_SEL_MAX_BLOCKS <= (1LL << dssel::kPositionBits),
+              "the score kernel tags staged positions with their row above bit 26");
 
 namespace {
 

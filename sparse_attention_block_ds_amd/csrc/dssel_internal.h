@@ -34,6 +34,7 @@ constexpr int kScorePieceMin = 64;           // and at least
 constexpr int kScoreWgsPerCu = 4;            // resident score workgroups per compute unit
 constexpr int kWaveStage = 512;              // per-wave candidate staging, all rows (LDS)
 constexpr int kCountPad = 32;                // candidate counters sit 128 bytes apart
+constexpr int kPositionBits = 26;            // staged candidates tag the row above the position
 
 constexpr int kSelectBuf = 8192;             // candidates the select holds in registers
 constexpr int kGatherSlack = 64;             // radix passes stop once m + this many words remain

@@ -57,7 +57,7 @@ __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
 }
 
 // A staged candidate: its key and its layer position, tagged with its row.
-constexpr int kRowShift = 26;  // positions are below 2^26 (DS_SEL_MAX_BLOCKS)
+constexpr int kRowShift = kPositionBits;  // positions are below 2^26 (the block limit)
 static_assert(kMaxRows <= 32, "row tag must fit above the position bits");
 
 template <int R>
@@ -383,10 +383,12 @@ __device__ Piece find_piece(const Call& c, int* shared_out) {
   const int lane = lane_id();
   if (threadIdx.x < kWave) {
     const int L = c.layers;
+    // the first 64 layers' counts stay in a register for the search below
+    const int n0 = lane < L ? c.counts[(int64_t)lane * kCountStride + kMaxRows] : 0;
     int64_t total = 0;
     for (int l0 = 0; l0 < L; l0 += kWave) {
       const int l = l0 + lane;
-      int64_t n = l < L ? c.counts[(int64_t)l * kCountStride + kMaxRows] : 0;
+      int64_t n = l0 == 0 ? n0 : (l < L ? c.counts[(int64_t)l * kCountStride + kMaxRows] : 0);
 #pragma unroll
       for (int off = kWave / 2; off > 0; off >>= 1) n += __shfl_xor(n, off, kWave);
       total += n;
@@ -398,7 +400,7 @@ __device__ Piece find_piece(const Call& c, int* shared_out) {
     int base = 0, layer = -1, pj = 0, pn = 0;
     for (int l0 = 0; l0 < L && layer < 0; l0 += kWave) {
       const int l = l0 + lane;
-      const int n = l < L ? c.counts[(int64_t)l * kCountStride + kMaxRows] : 0;
+      const int n = l0 == 0 ? n0 : (l < L ? c.counts[(int64_t)l * kCountStride + kMaxRows] : 0);
       const int g = (n + T - 1) / T;
       const int incl = wave_inclusive_scan(g);
       const bool mine = j >= base + incl - g && j < base + incl;
