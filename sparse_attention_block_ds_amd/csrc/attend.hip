@@ -49,9 +49,9 @@ struct AttendShared {
   static constexpr int kRowK = D + 8;       // halves per K row (16-byte pad: no bank conflicts)
   static constexpr int kRowV = kChunk + 8;  // halves per transposed V row
   static constexpr int kRowP = kChunk + 4;  // floats per weight row
-  uint16_t k[kChunk * kRowK];
-  uint16_t vt[D * kRowV];
-  float p[kThreads / kWave][16 * kRowP];    // per wave: its heads' weights for the chunk
+  alignas(16) uint16_t k[kChunk * kRowK];
+  alignas(16) uint16_t vt[D * kRowV];
+  alignas(16) float p[kThreads / kWave][16 * kRowP];  // per wave: its heads' weights for the chunk
   int32_t blk[kAttendMaxK];                 // the split's block indices, -1 where masked
 };
 
@@ -104,7 +104,8 @@ struct ChunkRegs {
     for (int t = 0; t < kKPer; ++t) {
       const int u = tid + t * kThreads;
       if (u < kKTasks)
-        *reinterpret_cast<u32x4_t*>(&sh.k[(u / kSegs) * S::kRowK + (u % kSegs) * 8]) = kv[t];
+        *static_cast<u32x4_t*>(__builtin_assume_aligned(&sh.k[(u / kSegs) * S::kRowK + (u % kSegs) * 8], 16)) =
+            kv[t];
     }
 #pragma unroll
     for (int t = 0; t < kVPer; ++t) {
@@ -198,8 +199,8 @@ __global__ __launch_bounds__(kThreads) void attend_partial_kernel(AttendCall c) 
       s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < KC; ++cc) {
-        const u32x4_t kb = *reinterpret_cast<const u32x4_t*>(
-            &sh.k[(16 * t + (lane & 15)) * S::kRowK + 32 * cc + 8 * (lane >> 4)]);
+        const u32x4_t kb = *static_cast<const u32x4_t*>(__builtin_assume_aligned(
+            &sh.k[(16 * t + (lane & 15)) * S::kRowK + 32 * cc + 8 * (lane >> 4)], 16));
         s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[cc], __builtin_bit_cast(bf16x8_t, kb), s[t],
                                                        0, 0, 0);
       }
@@ -242,8 +243,8 @@ __global__ __launch_bounds__(kThreads) void attend_partial_kernel(AttendCall c) 
 #pragma unroll
     for (int kk = 0; kk < kChunk / 32; ++kk) {
       const float* pr = pw + (lane & 15) * S::kRowP + 32 * kk + 8 * (lane >> 4);
-      const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(pr);
-      const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(pr + 4);
+      const f32x4_t p0 = *static_cast<const f32x4_t*>(__builtin_assume_aligned(pr, 16));
+      const f32x4_t p1 = *static_cast<const f32x4_t*>(__builtin_assume_aligned(pr + 4, 16));
       const float pe[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       u32x4_t hi, lo;
 #pragma unroll
@@ -257,8 +258,8 @@ __global__ __launch_bounds__(kThreads) void attend_partial_kernel(AttendCall c) 
       const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, hi), alo = __builtin_bit_cast(bf16x8_t, lo);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const u32x4_t vbits = *reinterpret_cast<const u32x4_t*>(
-            &sh.vt[(16 * n + (lane & 15)) * S::kRowV + 32 * kk + 8 * (lane >> 4)]);
+        const u32x4_t vbits = *static_cast<const u32x4_t*>(__builtin_assume_aligned(
+            &sh.vt[(16 * n + (lane & 15)) * S::kRowV + 32 * kk + 8 * (lane >> 4)], 16));
         const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, vbits);
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, o[n], 0, 0, 0);
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, o[n], 0, 0, 0);
