@@ -190,13 +190,13 @@ def attend_leg(p, selector, keys, idx, count, steps, warmup, stream):
     values = torch.randn((L, N, d), generator=g, device="cuda:0").to(torch.bfloat16)
     out = torch.empty((L, R, H, d), dtype=torch.float32, device="cuda:0")
     for _ in range(warmup):
-        selector.attend(qa, keys, values, idx, count, out=out, stream=stream)
+        selector.attend(qa, keys, values, idx, count, 1.0 / np.sqrt(d), out=out, stream=stream)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for a, b in evs:
         a.record(stream)
-        selector.attend(qa, keys, values, idx, count, out=out, stream=stream)
+        selector.attend(qa, keys, values, idx, count, 1.0 / np.sqrt(d), out=out, stream=stream)
         b.record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))

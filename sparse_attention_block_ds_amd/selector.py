@@ -122,8 +122,94 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on(t, device, name):
+    _require(t.device == device, f"{name} is on {t.device}, the handle is on {device}")
+
+
+def check_select_tensors(q, w, keys, k, mask=None, limit=None, out=None, device=None):
+    """Reject, before anything reaches the library, tensors whose dtype, shape,
+    strides or device differ from what ds_sel_score_select reads and writes.
+    Raises ValueError; returns nothing."""
+    import torch
+    _require(isinstance(k, int) and k >= 1, "k must be an int >= 1")
+    _require(q.dim() == 4 and q.dtype == torch.bfloat16 and q.is_contiguous(),
+             "q must be a contiguous bf16 tensor [L, R, H, d]")
+    device = q.device if device is None else torch.device(device)
+    L, R, H, d = q.shape
+    _require(w.dtype == torch.bfloat16 and tuple(w.shape) == (L, R, H) and w.is_contiguous(),
+             "w must be a contiguous bf16 tensor [L, R, H]")
+    _require(keys.dtype == torch.bfloat16 and keys.dim() == 3 and keys.shape[0] == L and
+             keys.shape[2] >= d and keys.stride(2) == 1,
+             "keys must be a bf16 tensor [L, N, ldk] with ldk >= d and unit stride in the last dim")
+    if keys.shape[1] > 1:
+        _require(keys.stride(1) >= d, "keys rows overlap (stride(1) < d)")
+    N = keys.shape[1]
+    tensors = [(q, "q"), (w, "w"), (keys, "keys")]
+    if mask is not None:
+        _require(mask.dtype == torch.int32 and mask.dim() == 3 and mask.shape[0] == L and
+                 mask.shape[1] in (1, R) and mask.shape[2] * 32 >= N and mask.stride(2) == 1,
+                 "mask must be an int32 tensor [L, R or 1, >= ceil(N/32)] with unit stride in the "
+                 "last dim")
+        tensors.append((mask, "mask"))
+    if limit is not None:
+        _require(limit.dtype == torch.int32 and tuple(limit.shape) == (L, R) and limit.is_contiguous(),
+                 "limit must be a contiguous int32 tensor [L, R]")
+        tensors.append((limit, "limit"))
+    if out is not None:
+        _require(isinstance(out, (tuple, list)) and len(out) == 3,
+                 "out must be (idx, score, count) with count possibly None")
+        idx, score, count = out
+        _require(idx is not None and idx.dtype == torch.int32 and tuple(idx.shape) == (L, R, k) and
+                 idx.is_contiguous(), "out idx must be a contiguous int32 tensor [L, R, k]")
+        _require(score is not None and score.dtype == torch.float32 and
+                 tuple(score.shape) == (L, R, k) and score.is_contiguous(),
+                 "out score must be a contiguous float32 tensor [L, R, k]")
+        tensors += [(idx, "out idx"), (score, "out score")]
+        if count is not None:
+            _require(count.dtype == torch.int32 and tuple(count.shape) == (L, R) and
+                     count.is_contiguous(), "out count must be a contiguous int32 tensor [L, R]")
+            tensors.append((count, "out count"))
+    for t, name in tensors:
+        _on(t, device, name)
+
+
+def check_attend_tensors(qa, keys, values, idx, count, scale, out=None, device=None):
+    """The same for ds_sel_attend.  Raises ValueError."""
+    import math
+    import torch
+    _require(isinstance(scale, (int, float)) and math.isfinite(float(scale)),
+             "scale must be a finite number (the library applies no default)")
+    _require(qa.dim() == 4 and qa.dtype == torch.bfloat16 and qa.is_contiguous(),
+             "qa must be a contiguous bf16 tensor [L, R, Ha, d]")
+    device = qa.device if device is None else torch.device(device)
+    L, R, Ha, d = qa.shape
+    for t, name in ((keys, "keys"), (values, "values")):
+        _require(t.dtype == torch.bfloat16 and t.dim() == 3 and t.shape[0] == L and
+                 t.shape[2] >= d and t.stride(2) == 1,
+                 f"{name} must be a bf16 tensor [L, N, ld] with ld >= d and unit stride in the last dim")
+    _require(keys.shape[1] == values.shape[1], "keys and values must hold the same number of blocks")
+    _require(idx.dtype == torch.int32 and idx.dim() == 3 and tuple(idx.shape[:2]) == (L, R) and
+             idx.is_contiguous(), "idx must be a contiguous int32 tensor [L, R, k]")
+    tensors = [(qa, "qa"), (keys, "keys"), (values, "values"), (idx, "idx")]
+    if count is not None:
+        _require(count.dtype == torch.int32 and tuple(count.shape) == (L, R) and count.is_contiguous(),
+                 "count must be a contiguous int32 tensor [L, R]")
+        tensors.append((count, "count"))
+    if out is not None:
+        _require(out.dtype == torch.float32 and tuple(out.shape) == (L, R, Ha, d) and
+                 out.is_contiguous(), "out must be a contiguous float32 tensor [L, R, Ha, d]")
+        tensors.append((out, "out"))
+    for t, name in tensors:
+        _on(t, device, name)
+
+
 def make_args(q, w, keys, k, mask=None, limit=None, out_idx=None, out_score=None, out_count=None):
-    """Fill an Args struct from tensors (no checks beyond shapes; the library validates)."""
+    """Fill an Args struct from tensors already accepted by check_select_tensors."""
     L, R, H, d = q.shape
     N = keys.shape[1]
     a = Args()
@@ -143,7 +229,7 @@ def make_args(q, w, keys, k, mask=None, limit=None, out_idx=None, out_score=None
 
 
 def make_attend_args(qa, keys, values, idx, count, scale, out):
-    """Fill an AttendArgs struct from tensors (no checks beyond shapes; the library validates)."""
+    """Fill an AttendArgs struct from tensors already accepted by check_attend_tensors."""
     L, R, H, d = qa.shape
     N = keys.shape[1]
     a = AttendArgs()
@@ -200,6 +286,8 @@ class Selector:
         recorded before prep and after prep, score and select.
         """
         torch = self._torch
+        dev = torch.device("cuda", self.device)
+        check_select_tensors(q, w, keys, k, mask, limit, out, dev)
         L, R = q.shape[0], q.shape[1]
         if out is None:
             out = (torch.empty((L, R, k), dtype=torch.int32, device=q.device),
@@ -223,16 +311,17 @@ class Selector:
         return out
 
 
-    def attend(self, qa, keys, values, idx, count=None, scale=None, out=None, stream=None):
+    def attend(self, qa, keys, values, idx, count, scale, out=None, stream=None):
         """Enqueue attention over a selection; returns out f32 [L,R,Ha,d].
 
         qa bf16 [L,R,Ha,d]; keys, values bf16 [L,N,ld] (unit stride in the last
         dim); idx int32 [L,R,k] and count int32 [L,R] or None, as score_select
-        returns them; scale defaults to 1/sqrt(d).  Asynchronous on `stream`.
+        returns them; scale is the caller's (1/sqrt(d) is the usual choice).
+        Asynchronous on `stream`.
         """
         torch = self._torch
-        if scale is None:
-            scale = 1.0 / float(qa.shape[3]) ** 0.5
+        check_attend_tensors(qa, keys, values, idx, count, scale, out,
+                             torch.device("cuda", self.device))
         if out is None:
             out = torch.empty(tuple(qa.shape), dtype=torch.float32, device=qa.device)
         a = make_attend_args(qa, keys, values, idx, count, scale, out)

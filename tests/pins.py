@@ -246,6 +246,33 @@ def check_metamorphic(lib):
         np.testing.assert_array_equal(x, y)
 
 
+def check_score_blocks(lib):
+    """The per-block scorer that judges general-input GPU results: over several
+    layers and rows, with per-row masks and limits, scoring every admitted block
+    must give bit for bit the scores the selection returns for k = N (which the
+    brute-force and exact-integer pins fix), and on integer inputs the exact
+    int64 scores."""
+    limits = np.array([[700, 650, 13, 699], [0, 700, 401, 522], [699, 1, 700, 350]], np.int32)
+    for values, seed in (("int3", 51), ("normal", 52)):
+        p = wl.make_custom(3, 4, 8, 64, 700, 700, seed=seed, values=values, mask_p=0.55,
+                           mask_shared=False, limits=limits)
+        idx, score, count = run(p, lib, k=p.blocks)
+        exact = exact_int_scores(p) if values == "int3" else None
+        adm = admitted_mask(p)
+        for l in range(p.layers):
+            for r in range(p.rows):
+                n = int(count[l, r])
+                assert n == int(adm[l, r].sum())
+                blocks = np.flatnonzero(adm[l, r]).astype(np.int32)
+                got = oracle.score_blocks(p.q, p.w, p.keys, l, r, blocks, lib=lib)
+                by_block = dict(zip(idx[l, r, :n].tolist(), score[l, r, :n].tolist()))
+                want = np.array([by_block[b] for b in blocks.tolist()], np.float32)
+                np.testing.assert_array_equal(got, want, err_msg=f"score_blocks l={l} r={r}")
+                if exact is not None:
+                    np.testing.assert_array_equal(got, exact[l, r, blocks].astype(np.float32),
+                                                  err_msg=f"score_blocks exact l={l} r={r}")
+
+
 # ------------------------------------------------------------------ attention
 def _bits(a):
     return wl.f32_to_bf16_bits(np.asarray(a, np.float32))
@@ -353,6 +380,7 @@ def all_pins(lib, include_slow=False):
                                     mask_p=0.5), lib)
     check_special_cases(lib)
     check_metamorphic(lib)
+    check_score_blocks(lib)
     check_attend(lib)
     if include_slow:
         check_exact_integer(wl.make("tiny"), lib)

@@ -1,0 +1,122 @@
+"""The binding's argument checks, on CPU tensors (no library call is made):
+every tensor whose dtype, shape, strides or device differs from what the C ABI
+reads or writes is rejected with ValueError before anything is enqueued."""
+import pytest
+import torch
+
+from sparse_attention_block_ds_amd import selector as sel
+
+L, R, H, D, N, K = 2, 3, 4, 64, 100, 16
+BF = torch.bfloat16
+CPU = torch.device("cpu")
+
+
+def good():
+    return dict(q=torch.zeros(L, R, H, D, dtype=BF), w=torch.zeros(L, R, H, dtype=BF),
+                keys=torch.zeros(L, N, D, dtype=BF), k=K,
+                mask=torch.zeros(L, 1, 4, dtype=torch.int32),
+                limit=torch.zeros(L, R, dtype=torch.int32),
+                out=(torch.zeros(L, R, K, dtype=torch.int32), torch.zeros(L, R, K),
+                     torch.zeros(L, R, dtype=torch.int32)))
+
+
+def check(**kw):
+    a = good()
+    a.update(kw)
+    sel.check_select_tensors(a["q"], a["w"], a["keys"], a["k"], a["mask"], a["limit"], a["out"], CPU)
+
+
+def test_accepts_well_formed():
+    check()
+    check(mask=None, limit=None, out=None)
+    check(keys=torch.zeros(L, N, 72, dtype=BF)[:, :, :D])          # padded rows
+    check(mask=torch.zeros(L, R, 4, dtype=torch.int32))           # a mask row per query row
+    o = good()["out"]
+    check(out=(o[0], o[1], None))
+
+
+@pytest.mark.parametrize("name,value", [
+    ("q", torch.zeros(L, R, H, D)),                                   # fp32, not bf16
+    ("q", torch.zeros(L, 2 * R, H, D, dtype=BF)[:, :R]),              # sliced rows: not contiguous
+    ("q", torch.zeros(L, R, H * D, dtype=BF)),                        # wrong rank
+    ("w", torch.zeros(L, R, H + 1, dtype=BF)),
+    ("w", torch.zeros(L, R, H, dtype=torch.float16)),
+    ("keys", torch.zeros(L, N, D)),
+    ("keys", torch.zeros(L, N, 2 * D, dtype=BF)[:, :, ::2]),         # non-unit last stride
+    ("keys", torch.zeros(L + 1, N, D, dtype=BF)),
+    ("keys", torch.zeros(L, N, D - 8, dtype=BF)),                     # rows shorter than d
+    ("mask", torch.zeros(L, 1, 3, dtype=torch.int32)),                # fewer than ceil(N/32) words
+    ("mask", torch.zeros(L, 2, 4, dtype=torch.int32)),                # neither 1 nor R rows
+    ("mask", torch.zeros(L, 1, 4, dtype=torch.int64)),
+    ("limit", torch.zeros(L, R, dtype=torch.int64)),
+    ("limit", torch.zeros(R, L, dtype=torch.int32)),
+    ("k", 0),
+    ("k", 2.0),
+])
+def test_rejects_input(name, value):
+    with pytest.raises(ValueError):
+        check(**{name: value})
+
+
+def _outs(**kw):
+    o = dict(zip(("idx", "score", "count"), good()["out"]))
+    o.update(kw)
+    return (o["idx"], o["score"], o["count"])
+
+
+@pytest.mark.parametrize("out", [
+    _outs(idx=torch.zeros(L, R, K - 1, dtype=torch.int32)),        # too small: would be overrun
+    _outs(idx=torch.zeros(L, R, K)),                                # float, not int32
+    _outs(score=torch.zeros(L, R, K, dtype=torch.float64)),
+    _outs(score=torch.zeros(L, R, 2 * K)[:, :, :K]),                # not contiguous
+    _outs(count=torch.zeros(L, R + 1, dtype=torch.int32)),
+    (torch.zeros(L, R, K, dtype=torch.int32), torch.zeros(L, R, K)),  # not a triple
+])
+def test_rejects_output(out):
+    with pytest.raises(ValueError):
+        check(out=out)
+
+
+def test_rejects_other_device():
+    a = good()
+    with pytest.raises(ValueError):
+        sel.check_select_tensors(a["q"], a["w"], a["keys"], K, None, None, None, torch.device("meta"))
+    with pytest.raises(ValueError):
+        check(limit=torch.zeros(L, R, dtype=torch.int32, device="meta"))
+
+
+def attend_good():
+    return dict(qa=torch.zeros(L, R, H, D, dtype=BF), keys=torch.zeros(L, N, D, dtype=BF),
+                values=torch.zeros(L, N, D, dtype=BF), idx=torch.zeros(L, R, K, dtype=torch.int32),
+                count=torch.zeros(L, R, dtype=torch.int32), scale=0.125,
+                out=torch.zeros(L, R, H, D))
+
+
+def check_attend(**kw):
+    a = attend_good()
+    a.update(kw)
+    sel.check_attend_tensors(a["qa"], a["keys"], a["values"], a["idx"], a["count"], a["scale"],
+                             a["out"], CPU)
+
+
+def test_attend_accepts_well_formed():
+    check_attend()
+    check_attend(count=None, out=None)
+
+
+@pytest.mark.parametrize("name,value", [
+    ("scale", None), ("scale", float("nan")), ("scale", float("inf")),
+    ("qa", torch.zeros(L, R, H, D)),
+    ("qa", torch.zeros(L, 2 * R, H, D, dtype=BF)[:, :R]),
+    ("values", torch.zeros(L, N + 1, D, dtype=BF)),
+    ("values", torch.zeros(L, N, D)),
+    ("keys", torch.zeros(L, N, 2 * D, dtype=BF)[:, :, ::2]),
+    ("idx", torch.zeros(L, R, K)),
+    ("idx", torch.zeros(L + 1, R, K, dtype=torch.int32)),
+    ("count", torch.zeros(L, R, dtype=torch.int64)),
+    ("out", torch.zeros(L, R, H, D - 1)),
+    ("out", torch.zeros(L, R, H, D, dtype=torch.float64)),
+])
+def test_attend_rejects(name, value):
+    with pytest.raises(ValueError):
+        check_attend(**{name: value})

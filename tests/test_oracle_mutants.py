@@ -29,6 +29,12 @@ MUTANTS = [
     ("wrong_row_of_w", "const uint16_t* w_row = w + lr * heads;", "const uint16_t* w_row = w + (int64_t)l * rows * heads;"),
     ("shared_mask_ignores_row", "mask + l * mask_layer_stride + r * mask_row_stride",
      "mask + l * mask_layer_stride"),
+    ("score_blocks_no_layer_stride", "keys + layer * key_layer_stride + (int64_t)list[j] * ldk",
+     "keys + (int64_t)list[j] * ldk"),
+    ("score_blocks_row_offset", "int64_t lr = (int64_t)layer * rows + row;",
+     "int64_t lr = (int64_t)row;"),
+    ("score_blocks_layer_as_row", "int64_t lr = (int64_t)layer * rows + row;",
+     "int64_t lr = (int64_t)row * rows + layer;"),
     ("attend_no_max_shift", "const double p = exp(s[j] - smax);", "const double p = exp(s[j]);"),
     ("attend_value_of_slot", "V + (int64_t)sel[j] * ldv", "V + (int64_t)j * ldv"),
     ("attend_key_of_slot", "K + (int64_t)sel[j] * ldk", "K + (int64_t)j * ldk"),
