@@ -3,30 +3,40 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sweep]
 
-A step is one call of the whole chain (admission + compaction + fold +
-candidate floors, the shared key stream that scores every admitted block for
-every row and keeps the keys at or above each row's floor, the bounded radix
-select with the ordered output) over one batch of synthetic input that is
-already resident in HBM.  The default workload is the 43-layer sweep at 300k
-context (43 layers x 6 verify rows x 75,000 compressed blocks, d = 128,
-H = 64, k = 512), whose 826 MB of keys exceed the 256 MB Infinity Cache, so
-every step streams its admitted keys from HBM.  Single-layer workloads
-(`--workload 300k|verify|8k|tiny`) rotate enough copies of their inputs that
-no copy is re-read while it could still sit in the Infinity Cache.
+A step is one call of the whole chain (admission + compaction, head-weight
+fold, candidate floors, the shared key stream that scores every admitted block
+for every row, the bounded radix select with the ordered output) over one
+batch of synthetic input already resident in HBM.  The default workload is the
+43-layer sweep at 300k context (43 layers x 6 verify rows x 75,000 compressed
+blocks, d = 128, H = 64, k = 512).
 
-Prints one JSON line on stdout: the candidate-block rate (sum over layers and
-rows of admitted blocks, per second), the key-stream kernel's achieved HBM
-bandwidth against the 8 TB/s peak (its algorithmic bytes: 2d bytes per
-union-admitted block, divided by its mean duration from HIP events recorded
-around it on its own stream), and the CPU oracle timed on a bounded sample
-of the same workload on this host, whose outputs are also compared with the
-GPU's before anything is printed.
+Cold discipline: enough distinct copies of the inputs are rotated that at
+least 512 MB (twice the 256 MB Infinity Cache) of algorithmic bytes are
+touched between two uses of one copy, so no step can be served from the cache.
+
+Prints one JSON line on stdout.  Besides the contract's keys it carries:
+  roofline       the chain's algorithmic bytes per step over its device time
+                 per step (HIP events around back-to-back steps), against the
+                 8 TB/s HBM peak; `traffic` from the committed rocprofv3
+                 counters when they were taken on the current kernel sources;
+  ceiling        calibration launches on the same inputs: an empty kernel, a
+                 plain read of every key row, a gather of exactly the admitted
+                 rows with the key stream's addressing;
+  single_calls   the 300k and 6-row verify configs as single calls, and the
+                 300k config batched 43 layers to a call: median, p10 and p90 of
+                 the per-call device time over event-bracketed calls, per-kernel
+                 medians, the chain's fraction of the HBM peak, parity;
+  cpu_baseline   the oracle timed on one host core on whole selections of the
+                 workload (outputs compared with the GPU's), with the host's CPU
+                 model and core count;
+  attend         attention over the last step's selection (not part of value).
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -36,8 +46,19 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
+COLD_BYTES = 2 * MALL_BYTES
 PROFILES = os.path.join(ROOT, "profiles")
-SCORE_SOURCE = os.path.join(ROOT, "sparse_attention_block_ds_amd", "csrc", "score.hip")
+CSRC = os.path.join(ROOT, "sparse_attention_block_ds_amd", "csrc")
+METRIC = "candidate blocks selected/sec per layer-row; achieved HBM GB/s vs peak"
+WORKLOADS = {
+    "sweep": "43-layer sweep at 300k context: 43 layers x 6 verify rows x 75,000 blocks",
+    "300k": "300k-context decode: 1 row x 75,000 blocks, mask p=0.6",
+    "300k_x43": "300k-context decode batched: 43 layers x 1 row x 75,000 blocks, mask p=0.6",
+    "verify": "6-row verify: 6 rows x 32,768 blocks",
+    "verify_int": "6-row verify, integer values: 6 rows x 32,768 blocks",
+    "8k": "8k-context decode: 1 row x 2,048 blocks",
+    "tiny": "tiny: 1 row x 4,096 blocks, H=4, d=64",
+}
 
 
 def log(*a):
@@ -49,15 +70,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "300k", "verify", "verify_int",
-                                                            "8k", "tiny"])
+    ap.add_argument("--workload", default="sweep", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--engine", default="mfma", choices=["mfma", "valu"],
                     help="key-stream engine: bf16 matrix cores (default) or fp32 vector FMAs")
-    ap.add_argument("--no-attend", action="store_true",
-                    help="skip the attention-over-the-selection leg")
+    ap.add_argument("--no-attend", action="store_true", help="skip the attention leg")
+    ap.add_argument("--no-singles", action="store_true", help="skip the single-call legs")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the calibration launches")
+    ap.add_argument("--calls", type=int, default=200,
+                    help="event-bracketed calls per single-call leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB read + 1 GiB write elementwise kernel, to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters")
@@ -78,31 +101,55 @@ def copy_calibration():
                       "launches": 3}), flush=True)
 
 
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def sources_sha256():
+    """One digest over every library source, so counters taken on other sources are not used."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
 def admitted_counts(p):
-    """Admitted blocks per (layer, row) and union-admitted blocks per layer (host numpy)."""
+    """Admitted blocks per (layer, row) and the union-admitted bits per layer (host numpy)."""
     import numpy as np
     L, R, N = p.layers, p.rows, p.blocks
     lim = np.full((L, R), N, np.int64) if p.limit is None else np.clip(p.limit.astype(np.int64), 0, N)
+    below = np.arange(N)[None, :]
     if p.mask is None:
-        return lim, lim.max(axis=1)
+        ubits = below < lim.max(axis=1)[:, None]
+        return lim, ubits
     bits = np.unpackbits(p.mask.view(np.uint8), axis=-1, bitorder="little")[..., :N].astype(bool)
     per_row = np.zeros((L, R), np.int64)
-    union = np.zeros(L, np.int64)
+    ubits = np.zeros((L, N), bool)
     for l in range(L):
-        u = np.zeros(N, bool)
         for r in range(R):
-            row_bits = bits[l, 0 if bits.shape[1] == 1 else r]
-            adm = row_bits & (np.arange(N) < lim[l, r])
+            adm = bits[l, 0 if bits.shape[1] == 1 else r] & (below[0] < lim[l, r])
             per_row[l, r] = adm.sum()
-            u |= adm
-        union[l] = u.sum()
-    return per_row, union
+            ubits[l] |= adm
+    return per_row, ubits
 
 
-def algorithmic_bytes(p, union):
-    """Bytes the method itself must move per call (intermediates excluded)."""
+def algorithmic_bytes(p, union_count):
+    """Bytes the method itself must move per call (intermediates excluded): the
+    union-admitted key rows (2d bytes each, read once for all rows), the mask,
+    q and w, the limits and the outputs."""
     import numpy as np
-    keys = int(union.sum()) * 2 * p.dim
+    keys = int(union_count) * 2 * p.dim
     mask = 0 if p.mask is None else int(np.prod(p.mask.shape)) * 4
     qw = p.layers * p.rows * p.heads * (p.dim + 1) * 2
     lim = 0 if p.limit is None else p.layers * p.rows * 4
@@ -111,112 +158,320 @@ def algorithmic_bytes(p, union):
 
 
 def load_traffic(workload):
-    """Counter-measured HBM bytes per score launch, if taken on the current kernel source."""
-    path = os.path.join(PROFILES, f"score_{workload}_pmc.json")
+    """Counter-measured HBM bytes per launch, if taken on the current library sources."""
+    path = os.path.join(PROFILES, f"chain_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(SCORE_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("score_source_sha256") != sha:
+    if rec.get("sources_sha256") != sources_sha256():
         return None
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(p, gpu_out, budget_s):
-    """Time the oracle (one thread, as written) on whole (layer, row) selections of
-    this workload until about budget_s seconds have been spent; check the GPU's
-    outputs for those selections against it."""
+def pct(xs):
+    import numpy as np
+    a = np.asarray(xs, np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90))}
+
+
+class Runner:
+    """One workload on the device: rotated input copies, outputs, a handle."""
+
+    def __init__(self, p, engine, stream, sets=None):
+        import numpy as np
+        import torch
+        from sparse_attention_block_ds_amd import selector as sel
+        self.p = p
+        self.stream = stream
+        self.per_row, self.ubits = admitted_counts(p)
+        self.alg = algorithmic_bytes(p, self.ubits.sum())
+        n = max(2, math.ceil(COLD_BYTES / self.alg["total"])) if sets is None else sets
+        first = sel.upload(p, "cuda:0")
+        self.sets = [first] + [tuple(None if t is None else t.clone() for t in first)
+                               for _ in range(n - 1)]
+        self.n_sets = n
+        self.selector = sel.Selector(max_layers=p.layers, max_rows=p.rows, max_heads=p.heads,
+                                     max_dim=p.dim, max_blocks=p.blocks, max_k=p.k, device=0,
+                                     engine=engine)
+        L, R, k = p.layers, p.rows, p.k
+        self.outs = [(torch.empty((L, R, k), dtype=torch.int32, device="cuda:0"),
+                      torch.empty((L, R, k), dtype=torch.float32, device="cuda:0"),
+                      torch.empty((L, R), dtype=torch.int32, device="cuda:0"))
+                     for _ in range(n)]
+        self.candidates = int(np.asarray(self.per_row).sum())
+        torch.cuda.synchronize()
+
+    def step(self, i, events=None):
+        q, w, keys, mask, limit = self.sets[i % self.n_sets]
+        self.selector.score_select(q, w, keys, self.p.k, mask, limit, out=self.outs[i % self.n_sets],
+                                   stream=self.stream, events=events)
+
+    def output(self, i):
+        return tuple(t.cpu().numpy() for t in self.outs[i % self.n_sets])
+
+    def close(self):
+        self.selector.close()
+
+
+def time_back_to_back(run, steps, warmup):
+    """Wall and device milliseconds per step over `steps` back-to-back steps."""
+    import torch
+    for i in range(warmup):
+        run.step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(run.stream)
+    for i in range(steps):
+        run.step(i)
+    b.record(run.stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1000.0 / steps
+    return wall, a.elapsed_time(b) / steps
+
+
+def per_call(run, calls):
+    """Per-call device time (events right before and after each call, calls
+    back to back) and per-kernel device times from the profiled entry point."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for i, (a, b) in enumerate(evs):
+        a.record(run.stream)
+        run.step(i)
+        b.record(run.stream)
+    torch.cuda.synchronize()
+    call_us = [a.elapsed_time(b) * 1000.0 for a, b in evs]
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(calls)]
+    for i in range(calls):
+        run.step(i, kev[i])
+    torch.cuda.synchronize()
+    names = ("prep", "score", "select")
+    kernels = {n: pct([e[j].elapsed_time(e[j + 1]) * 1000.0 for e in kev])["median"]
+               for j, n in enumerate(names)}
+    return pct(call_us), kernels
+
+
+def _sub_problem(p, l, r):
+    from sparse_attention_block_ds_amd import workloads as wl
+    mrow = 0 if p.mask is None or p.mask.shape[1] == 1 else r
+    return wl.Problem("s", p.k, p.q[l:l + 1, r:r + 1], p.w[l:l + 1, r:r + 1], p.keys[l:l + 1],
+                      None if p.mask is None else p.mask[l:l + 1, mrow:mrow + 1],
+                      None if p.limit is None else p.limit[l:l + 1, r:r + 1])
+
+
+def _accept(p, sub, out, l, r, ora, lib):
+    """The acceptance rule for one (layer, row): bit-exact on integer inputs;
+    otherwise count exact, every returned score within 1e-6 + 1e-5 |oracle
+    score of that block|, and every selected block's oracle score >= oracle
+    m-th score - 1e-4 max |score|."""
     import numpy as np
     import oracle
-    from sparse_attention_block_ds_amd import workloads as wl
+    g_idx, g_score, g_count = out
+    o_idx, o_score, o_count = ora
+    if p.integer_valued:
+        return (np.array_equal(o_idx[0, 0], g_idx[l, r]) and
+                np.array_equal(o_score[0, 0], g_score[l, r]) and o_count[0, 0] == g_count[l, r])
+    m = int(o_count[0, 0])
+    if g_count[l, r] != m or not np.all(g_idx[l, r, m:] == -1):
+        return False
+    if m == 0:
+        return True
+    s_or = oracle.score_blocks(sub.q, sub.w, sub.keys, 0, 0, g_idx[l, r, :m], lib=lib)
+    kth = float(o_score[0, 0, m - 1])
+    maxabs = max(abs(float(o_score[0, 0, 0])), abs(kth))
+    return (bool(np.all(np.abs(g_score[l, r, :m] - s_or) <= 1e-6 + 1e-5 * np.abs(s_or))) and
+            bool(np.all(s_or >= kth - 1e-4 * maxabs)))
 
+
+def check_parity(p, out, pairs):
+    """Number of (layer, row) pairs that fail the acceptance rule against the oracle."""
+    import oracle
     lib = oracle.load()
-    g_idx, g_score, g_count = gpu_out
+    bad = 0
+    for l, r in pairs:
+        sub = _sub_problem(p, l, r)
+        ora = oracle.select(sub.q, sub.w, sub.keys, sub.k, sub.mask, sub.limit, lib=lib)
+        bad += 0 if _accept(p, sub, out, l, r, ora, lib) else 1
+    return bad
+
+
+def cpu_baseline(p, gpu_out, budget_s, per_row):
+    """The oracle (one thread, as written, pinned to one core) on whole
+    (layer, row) selections of this workload until about budget_s seconds have
+    been spent; the GPU's outputs for those selections are checked against it."""
+    import oracle
+    lib = oracle.load()
     step = max(1, p.layers // 4)
     layers = list(range(0, p.layers, step)) + [l for l in range(p.layers) if l % step]
     order = [(l, r) for l in layers for r in range(p.rows)]
-    per_row, _ = admitted_counts(p)
-    done, cand, spent, mismatches = [], 0, 0.0, 0
-    for l, r in order:
-        mrow = 0 if p.mask is None or p.mask.shape[1] == 1 else r
-        sub = wl.Problem("s", p.k, p.q[l:l + 1, r:r + 1], p.w[l:l + 1, r:r + 1], p.keys[l:l + 1],
-                         None if p.mask is None else p.mask[l:l + 1, mrow:mrow + 1],
-                         None if p.limit is None else p.limit[l:l + 1, r:r + 1])
-        t0 = time.perf_counter()
-        o_idx, o_score, o_count = oracle.select(sub.q, sub.w, sub.keys, sub.k, sub.mask, sub.limit,
-                                                lib=lib)
-        spent += time.perf_counter() - t0
-        cand += int(per_row[l, r])
-        done.append((l, r))
-        if p.integer_valued:
-            same = (np.array_equal(o_idx[0, 0], g_idx[l, r]) and
-                    np.array_equal(o_score[0, 0], g_score[l, r]) and o_count[0, 0] == g_count[l, r])
-        else:
-            m = int(o_count[0, 0])
-            s_or = oracle.score_blocks(sub.q, sub.w, sub.keys, 0, 0, g_idx[l, r, :m], lib=lib)
-            kth = float(o_score[0, 0, m - 1]) if m else 0.0
-            maxabs = max(abs(float(o_score[0, 0, 0])), abs(kth)) if m else 0.0
-            same = (g_count[l, r] == m and bool(np.all(np.abs(g_score[l, r, :m] - s_or) <=
-                                                       1e-6 + 1e-5 * np.abs(s_or))) and
-                    bool(np.all(s_or >= kth - 1e-4 * maxabs)))
-        mismatches += 0 if same else 1
-        if spent >= budget_s:
-            break
+    prev = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(prev)})
+    done, cand, spent, bad = 0, 0, 0.0, 0
+    try:
+        for l, r in order:
+            sub = _sub_problem(p, l, r)
+            t0 = time.perf_counter()
+            ora = oracle.select(sub.q, sub.w, sub.keys, sub.k, sub.mask, sub.limit, lib=lib)
+            spent += time.perf_counter() - t0
+            cand += int(per_row[l, r])
+            done += 1
+            bad += 0 if _accept(p, sub, gpu_out, l, r, ora, lib) else 1
+            if spent >= budget_s:
+                break
+    finally:
+        os.sched_setaffinity(0, prev)
+    model, ncpu = host_cpu()
+    return {"value": cand / spent, "unit": "candidate blocks/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} whole (layer,row) selections of this workload "
+                      f"({cand} candidate blocks, {spent:.1f} s on one pinned core)",
+            "host_cpu": model, "host_cores": ncpu, "_bad": bad, "_checked": done}
+
+
+def balanced_ranges(ubits, groups):
+    """Flattened (layer * N + block) range starts that give every workgroup the
+    same number of union-admitted rows, with in-layer starts aligned to 32."""
+    import numpy as np
+    L, N = ubits.shape
+    cum = np.cumsum(ubits.reshape(-1))
+    total = int(cum[-1]) if cum.size else 0
+    targets = (np.arange(groups + 1, dtype=np.int64) * total) // groups
+    pos = np.searchsorted(cum, targets, side="left").astype(np.int64)
+    pos = pos - (pos % N) % 32
+    pos[0], pos[-1] = 0, L * N
+    return np.maximum.accumulate(pos)
+
+
+def ceiling(run, cus):
+    """Calibration launches on the first input copy: an empty kernel (256 and
+    4 x CU workgroups), a plain read of every key row, and the gather of the
+    union-admitted rows only (ranges balanced by admitted count)."""
+    import numpy as np
+    import torch
+    from sparse_attention_block_ds_amd import selector as sel
+    p = run.p
+    q, w, keys, mask, limit = run.sets[0]
+    G = 4 * cus
+    sink = torch.zeros(G, dtype=torch.int32, device="cuda:0")
+
+    def med_us(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(run.stream)
+            fn()
+            b.record(run.stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) * 1000.0 for a, b in evs]))
+
+    res = {}
+    for wg in (256, G):
+        res[f"empty_kernel_us_{wg}_wgs"] = med_us(
+            lambda: sel.calibrate(sel.DS_SEL_CALIB_EMPTY, wg, sink, stream=run.stream), 100)
+    packed = keys.shape[2] == p.dim
+    if packed:
+        nbytes = p.layers * p.blocks * p.dim * 2
+        us = med_us(lambda: sel.calibrate(sel.DS_SEL_CALIB_READ, G, sink, keys=keys,
+                                          stream=run.stream), 20)
+        res["read_all_rows"] = {"bytes": nbytes, "us": us, "gbs": nbytes / us / 1e3}
+    ranges = torch.from_numpy(balanced_ranges(run.ubits, G)).to("cuda:0")
+    gmask = None
+    if mask is not None and mask.shape[1] == 1:
+        gmask = mask
+    if mask is None or gmask is not None:
+        nbytes = int(run.ubits.sum()) * 2 * p.dim
+        us = med_us(lambda: sel.calibrate(sel.DS_SEL_CALIB_GATHER, G, sink, keys=keys, mask=gmask,
+                                          ranges=ranges, stream=run.stream), 20)
+        res["gather_admitted_rows"] = {"bytes": nbytes, "us": us, "gbs": nbytes / us / 1e3}
+    res["note"] = (f"median of event-timed launches of {G} workgroups x 256 threads "
+                   "(empty: also 256); the read and gather touch the same bytes as one step")
+    return res
+
+
+def single_leg(name, engine, stream, calls):
+    """One single-call config: per-call device-time percentiles, per-kernel
+    medians, back-to-back throughput, parity of sampled (layer, row) pairs."""
+    import numpy as np
+    from sparse_attention_block_ds_amd import workloads as wl
+    t0 = time.perf_counter()
+    p = wl.make(name)
+    run = Runner(p, engine, stream)
+    log(f"[bench] single-call leg {name}: {run.n_sets} input copies, generated+uploaded in "
+        f"{time.perf_counter() - t0:.1f}s")
+    wall_ms, dev_ms = time_back_to_back(run, calls, 10)
+    call_us, kernels = per_call(run, calls)
+    out = run.output(calls - 1)
+    pairs = [(l, r) for l in sorted({0, p.layers // 2, p.layers - 1}) for r in range(p.rows)]
+    # the last call used copy (calls - 1) % n_sets, whose values equal the host problem
+    bad = check_parity(p, out, pairs)
+    run.close()
+    if bad:
+        log(f"[bench] PARITY FAILURE in the {name} leg: {bad} of {len(pairs)} pairs")
+        sys.exit(3)
+    alg = run.alg["total"]
     return {
-        "value": cand / spent, "unit": "candidate blocks/s", "cores": 1, "kind": "oracle",
-        "sample": f"{len(done)} whole (layer,row) selections of this workload "
-                  f"({cand} candidate blocks, {spent:.1f} s single-threaded)",
-        "_mismatches": mismatches, "_checked": len(done),
+        "workload": WORKLOADS[name], "input_copies": run.n_sets,
+        "device_us_per_call": call_us,
+        "kernels_us_median": kernels,
+        "back_to_back_us_per_call": dev_ms * 1000.0,
+        "algorithmic_bytes": alg,
+        "chain_frac_hbm": alg / (call_us["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "chain_frac_hbm_back_to_back": alg / (dev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "candidate_blocks_per_s": run.candidates / (call_us["median"] * 1e-6),
+        "parity": f"{len(pairs)} (layer,row) pairs match the oracle "
+                  + ("bit-exact" if p.integer_valued else "(tolerance + set rule)"),
     }
 
 
-def attend_leg(p, selector, keys, idx, count, steps, warmup, stream):
-    """Attention over the chain's selection (64 query heads per row, bf16 q and
-    values drawn on the device from a fixed seed), timed with HIP events on the
-    launch stream; two (layer, row) pairs are checked against the fp64 oracle.
-
-    Algorithmic bytes per (layer, row): count x 2 x 2d (the selected K and V
-    rows) + H d 2 (q) + H d 4 (the fp32 output); flops: 4 H d per selected block."""
+def attend_leg(run, steps):
+    """Attention over the last step's selection (64 query heads per row, bf16 q
+    and values drawn on the device from a fixed seed), timed with HIP events on
+    the launch stream; two (layer, row) pairs are checked against the fp64
+    oracle.  Algorithmic bytes per (layer, row): count x 2 x 2d (the selected K
+    and V rows) + H d 2 (q) + H d 4 (the fp32 output); flops 4 H d per block."""
     import numpy as np
     import torch
     import oracle
-
+    p, stream = run.p, run.stream
+    i_last = steps - 1
+    keys = run.sets[i_last % run.n_sets][2]
+    idx, _, count = run.outs[i_last % run.n_sets]
     L, R, H, d, N = p.layers, p.rows, p.heads, p.dim, p.blocks
     g = torch.Generator(device="cuda:0")
     g.manual_seed(1234)
     qa = torch.randn((L, R, H, d), generator=g, device="cuda:0").to(torch.bfloat16)
     values = torch.randn((L, N, d), generator=g, device="cuda:0").to(torch.bfloat16)
     out = torch.empty((L, R, H, d), dtype=torch.float32, device="cuda:0")
-    for _ in range(warmup):
-        selector.attend(qa, keys, values, idx, count, 1.0 / np.sqrt(d), out=out, stream=stream)
+    scale = 1.0 / math.sqrt(d)
+    for _ in range(3):
+        run.selector.attend(qa, keys, values, idx, count, scale, out=out, stream=stream)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+           for _ in range(20)]
     for a, b in evs:
         a.record(stream)
-        selector.attend(qa, keys, values, idx, count, 1.0 / np.sqrt(d), out=out, stream=stream)
+        run.selector.attend(qa, keys, values, idx, count, scale, out=out, stream=stream)
         b.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
     cnt = count.cpu().numpy().astype(np.int64)
     sel_blocks = int(np.clip(cnt, 0, p.k).sum())
     nbytes = sel_blocks * 2 * 2 * d + L * R * H * d * (2 + 4)
     flops = 4.0 * H * d * sel_blocks
-    # parity sample: first and last (layer, row)
     bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
     worst = 0.0
     for l, r in ((0, 0), (L - 1, R - 1)):
         ref = oracle.attend(bits(qa[l:l + 1, r:r + 1]), bits(keys[l:l + 1]), bits(values[l:l + 1]),
                             idx[l:l + 1, r:r + 1].cpu().numpy(), count[l:l + 1, r:r + 1].cpu().numpy(),
-                            1.0 / np.sqrt(d))
+                            scale)
         err = np.abs(out[l:l + 1, r:r + 1].cpu().numpy() - ref).max() / max(np.abs(ref).max(), 1e-30)
         worst = max(worst, float(err))
     if not worst <= 1e-4:
         log(f"[bench] ATTENTION PARITY FAILURE: relative max error {worst:.3e}")
         sys.exit(3)
-    return {"kernel": "attend (softmax(q K^T) V over the selected blocks)", "ms": ms,
+    return {"kernel": "attend (softmax(q K^T) V over the selected blocks)", "us_median": ms * 1000.0,
             "selected_blocks": sel_blocks, "algorithmic_bytes": nbytes,
             "achieved_gbs": nbytes / (ms / 1000.0) / 1e9,
             "frac_hbm": nbytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
@@ -232,97 +487,71 @@ def main():
               "multi-GPU runs are not part of this build (see the sharding note in DESIGN.md).",
               file=sys.stderr)
         sys.exit(2)
-
     if args.copy_calibration:
         copy_calibration()
         return
 
     import numpy as np
     import torch
-    from sparse_attention_block_ds_amd import selector as sel
     from sparse_attention_block_ds_amd import workloads as wl
 
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
     torch.cuda.set_device(0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
     t_gen = time.perf_counter()
     p = wl.make(args.workload)
-    per_row, union = admitted_counts(p)
-    alg = algorithmic_bytes(p, union)
+    run = Runner(p, args.engine, stream)
     log(f"[bench] workload {p.name}: L={p.layers} R={p.rows} H={p.heads} d={p.dim} N={p.blocks} "
-        f"k={p.k}; candidates {int(per_row.sum())}; generated in {time.perf_counter() - t_gen:.1f}s")
+        f"k={p.k}; candidates {run.candidates}; {run.n_sets} input copies; "
+        f"ready in {time.perf_counter() - t_gen:.1f}s")
 
-    set_bytes = p.keys.nbytes
-    n_sets = 1 if set_bytes >= 2 * MALL_BYTES else int(np.ceil(2 * MALL_BYTES / set_bytes)) + 1
-    sets = [sel.upload(p, "cuda:0") for _ in range(n_sets)]
-    selector = sel.Selector(max_layers=p.layers, max_rows=p.rows, max_heads=p.heads,
-                            max_dim=p.dim, max_blocks=p.blocks, max_k=p.k, device=0,
-                            engine=args.engine)
-    outs = [(torch.empty((p.layers, p.rows, p.k), dtype=torch.int32, device="cuda:0"),
-             torch.empty((p.layers, p.rows, p.k), dtype=torch.float32, device="cuda:0"),
-             torch.empty((p.layers, p.rows), dtype=torch.int32, device="cuda:0"))
-            for _ in range(n_sets)]
-    stream = torch.cuda.current_stream()
+    # timed region: exactly K back-to-back steps
+    ms_per_step, dev_ms = time_back_to_back(run, args.steps, args.warmup)
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms wall, {dev_ms:.4f} ms device per step")
+    call_us, kernels = per_call(run, args.steps)
+    gpu_out = run.output(args.steps - 1)
 
-    def step(i, events=None):
-        q, w, keys, mask, limit = sets[i % n_sets]
-        selector.score_select(q, w, keys, p.k, mask, limit, out=outs[i % n_sets], stream=stream,
-                              events=events)
+    value = run.candidates / (ms_per_step / 1000.0)
+    achieved = run.alg["total"] / (dev_ms / 1000.0) / 1e9
+    score_gbs = run.alg["keys"] / (kernels["score"] * 1e-6) / 1e9
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region: exactly K steps
-    start_ev = torch.cuda.Event(enable_timing=True)
-    end_ev = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start_ev.record(stream)
-    for i in range(args.steps):
-        step(i)
-    end_ev.record(stream)
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    dev_ms = start_ev.elapsed_time(end_ev) / args.steps
-    ms_per_step = wall_s * 1000.0 / args.steps
-
-    # per-kernel ledger: HIP events around each kernel on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    score_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    select_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-
-    gpu_out = tuple(t.cpu().numpy() for t in outs[(args.steps - 1) % n_sets])
-    candidates = int(per_row.sum())
-    value = candidates / (ms_per_step / 1000.0)
-    achieved = alg["keys"] / (score_ms / 1000.0) / 1e9
-
-    cpu = None
+    cpu, parity = None, "not checked (--no-cpu-baseline)"
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(p, gpu_out, args.cpu_seconds)
-        if cpu["_mismatches"]:
-            log(f"[bench] PARITY FAILURE on {cpu['_mismatches']} of {cpu['_checked']} sampled selections")
+        cpu = cpu_baseline(p, gpu_out, args.cpu_seconds, run.per_row)
+        if cpu["_bad"]:
+            log(f"[bench] PARITY FAILURE on {cpu['_bad']} of {cpu['_checked']} sampled selections")
             sys.exit(3)
-        parity = f"{cpu['_checked']} sampled selections match the oracle " + \
+        parity = f"{cpu['_checked']} whole selections match the oracle " + \
                  ("bit-exact" if p.integer_valued else "(tolerance + set rule)")
         cpu = {k: v for k, v in cpu.items() if not k.startswith("_")}
-    else:
-        parity = "not checked (--no-cpu-baseline)"
+        log(f"[bench] cpu baseline done: {parity}")
 
+    ceil = None if args.no_ceiling else ceiling(run, cus)
+    if ceil:
+        log(f"[bench] ceiling: {json.dumps(ceil)}")
     attend = None
     if not args.no_attend and p.heads >= 16:
-        last = outs[(args.steps - 1) % n_sets]
-        attend = attend_leg(p, selector, sets[(args.steps - 1) % n_sets][2], last[0], last[2],
-                            min(args.steps, 20), 3, stream)
+        attend = attend_leg(run, args.steps)
+        log("[bench] attention leg done")
+    candidates, n_sets, alg = run.candidates, run.n_sets, run.alg
+    run.close()
+    del run
+    torch.cuda.empty_cache()
+
+    singles = None
+    if not args.no_singles and args.workload == "sweep":
+        singles = {}
+        for name in ("300k", "verify", "300k_x43"):
+            singles[name] = single_leg(name, args.engine, stream, args.calls)
+            log(f"[bench] {name}: {json.dumps(singles[name]['device_us_per_call'])} us per call")
+            torch.cuda.empty_cache()
 
     traffic = load_traffic(p.name)
     line = {
-        "metric": "candidate blocks selected/sec per layer-row; achieved HBM GB/s vs peak",
+        "metric": METRIC,
         "value": value,
         "unit": "candidate blocks/s",
         "n_gpus": 1,
@@ -335,33 +564,31 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": {
-                "sweep": "43-layer sweep at 300k context: 43 layers x 6 verify rows x 75,000 blocks",
-                "300k": "300k-context decode: 1 row x 75,000 blocks, mask p=0.6",
-                "verify": "6-row verify: 6 rows x 32,768 blocks",
-                "verify_int": "6-row verify, integer values: 6 rows x 32,768 blocks",
-                "8k": "8k-context decode: 1 row x 2,048 blocks",
-                "tiny": "tiny: 1 row x 4,096 blocks, H=4, d=64",
-            }[p.name],
+            "workload": WORKLOADS[p.name],
             "layers": p.layers, "rows": p.rows, "heads": p.heads, "dim": p.dim,
             "blocks": p.blocks, "k": p.k, "candidates_per_step": candidates,
-            "input_sets_rotated": n_sets, "engine": args.engine,
+            "input_copies_rotated": n_sets, "engine": args.engine,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": "score (shared key stream)",
+            "kernel": "chain (prep + score + select): algorithmic bytes per step / device time per step",
+            "algorithmic_bytes": alg["total"],
+            "score_kernel": {"algorithmic_key_bytes": alg["keys"],
+                             "us_median": kernels["score"], "gbs": score_gbs,
+                             "frac": score_gbs / HBM_PEAK_GBS},
         },
+        "ceiling": ceil,
         "cpu_baseline": cpu,
-        "kernels_ms": {"prep": prep_ms, "score": score_ms, "select": select_ms},
+        "kernels_us_median": kernels,
+        "device_us_per_call": call_us,
         "device_ms_per_step": dev_ms,
         "layer_row_selections_per_s": p.layers * p.rows / (ms_per_step / 1000.0),
-        "chain_algorithmic_gbs": alg["total"] / (ms_per_step / 1000.0) / 1e9,
         "parity": parity,
+        "single_calls": singles,
         "attend": attend,
     }
     print(json.dumps(line), flush=True)
-    selector.close()
 
 
 if __name__ == "__main__":

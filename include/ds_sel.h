@@ -194,7 +194,51 @@ int ds_sel_attend(ds_sel* h, const ds_sel_attend_args* a, void* hip_stream);
 /* The host-side checks ds_sel_attend applies, without a device. */
 int ds_sel_check_attend_args(const ds_sel_limits* lim, const ds_sel_attend_args* a);
 
-/* Free the handle and its scratch (waits for the device to finish using it).
+/* Calibration launches: the floors and ceilings the chain is measured
+ * against (the pages keep a per-dispatch bandwidth ledger for the same
+ * purpose: page "DeepSeek V4.1F Q4 on M3 Ultra with native DSpark MTP (40tps
+ * / 800tps)", the paragraph listing what else the repository holds).  None
+ * computes anything of the selection; each XOR-folds what it reads into
+ * sink[workgroup] so that no load is dropped.
+ *   DS_SEL_CALIB_EMPTY   an empty kernel on `workgroups` workgroups of 256 threads;
+ *   DS_SEL_CALIB_READ    reads every key row [0, N) x [0, dim) of every layer
+ *                        with 16-byte loads; the rows must be packed
+ *                        (ldk == dim, and key_layer_stride == N * dim when L > 1);
+ *   DS_SEL_CALIB_GATHER  reads exactly the key rows whose bit is set in the
+ *                        layer's mask row (all rows when mask is NULL), with the
+ *                        addressing the key stream uses; workgroup g takes the
+ *                        flattened (layer * N + block) range [ranges[g],
+ *                        ranges[g + 1]), whose in-layer starts must be multiples
+ *                        of 32 (DS_SEL_E_INVALID is not checked for this: the
+ *                        ranges live in device memory).
+ * Asynchronous on `hip_stream` on the current device; sink is device memory of
+ * at least `workgroups` words, ranges of workgroups + 1 int64 (gather only). */
+#define DS_SEL_CALIB_EMPTY 0
+#define DS_SEL_CALIB_READ 1
+#define DS_SEL_CALIB_GATHER 2
+
+typedef struct {
+  uint32_t struct_size;      /* sizeof(ds_sel_calib_args) */
+  int32_t kind;              /* DS_SEL_CALIB_* */
+  int32_t workgroups;        /* 1 .. 65535 */
+  int32_t layers;            /* L >= 1 (read, gather) */
+  int32_t dim;               /* d in {32, 64, 128, 256} (read, gather) */
+  int32_t reserved;          /* 0 */
+  int64_t blocks;            /* N >= 1 (read, gather) */
+  const void* keys;          /* bf16, as in ds_sel_args */
+  int64_t ldk, key_layer_stride;
+  const uint32_t* mask;      /* gather: NULL, or one row of ceil(N/32) words per layer */
+  int64_t mask_layer_stride; /* words */
+  const int64_t* ranges;     /* gather: int64 [workgroups + 1], device memory */
+  uint32_t* sink;            /* uint32 [workgroups], device memory */
+} ds_sel_calib_args;
+
+int ds_sel_calibrate(const ds_sel_calib_args* a, void* hip_stream);
+
+/* Free the handle and its scratch, after waiting for the handle's last
+ * enqueued call to finish (only that work: other streams and handles are not
+ * waited for).  Work captured into a graph is not tracked: a caller that
+ * replays such a graph must finish its replays before destroying the handle.
  * NULL is a no-op. */
 void ds_sel_destroy(ds_sel* h);
 

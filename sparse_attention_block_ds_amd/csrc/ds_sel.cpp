@@ -4,20 +4,12 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <new>
 
 #include "ds_sel.h"
 #include "dssel_internal.h"
 
-struct ds_sel {
-  ds_sel_limits lim;
-  void* scratch = nullptr;
-  int64_t scratch_bytes = 0;
-  int compute_units = 256;  // of the handle's device, read at create
-  // offsets into scratch
-  int64_t off_qt = 0, off_qparts = 0, off_list = 0, off_counts = 0, off_floor = 0, off_ccount = 0,
-          off_cand = 0, off_part_ml = 0, off_part_o = 0;
-};
 
 // The select orders at most 2048 winners per row in LDS.
 static_assert(DS_SEL_MAX_K <= 2048, "select kernel LDS sized for k <= 2048");
@@ -42,7 +34,7 @@ struct Layout {
 // [L][R][N rounded up to 4] (room for every position, so none is ever dropped);
 // then the attention's split records: (max, sum) and o[d] fp32 per head of a
 // 64-head tile, for at most kAttendPartialWgs workgroups.
-Layout layout_for(const ds_sel_limits& lim) {
+Layout layout_for(const ds_sel_limits& lim, bool with_attend = true) {
   Layout s{};
   const int64_t L = lim.max_layers, R = lim.max_rows, D = lim.max_dim, N = lim.max_blocks;
   int64_t off = 0;
@@ -53,12 +45,26 @@ Layout layout_for(const ds_sel_limits& lim) {
   s.floor = off;  off += align_up(L * R * 4);
   s.ccount = off; off += align_up(L * R * dssel::kCountPad * 4);
   s.cand = off;   off += align_up(L * R * ((N + 3) / 4 * 4) * 8);
-  const int64_t recs = (int64_t)dssel::kAttendPartialWgs * dssel::kAttendHeadTile;
-  s.part_ml = off; off += align_up(recs * 2 * 4);
-  s.part_o = off;  off += align_up(recs * D * 4);
+  if (with_attend) {
+    const int64_t recs = (int64_t)dssel::kAttendPartialWgs * dssel::kAttendHeadTile;
+    s.part_ml = off; off += align_up(recs * 2 * 4);
+    s.part_o = off;  off += align_up(recs * D * 4);
+  }
   s.total = off;
   return s;
 }
+
+}  // namespace
+
+struct ds_sel {
+  ds_sel_limits lim;
+  void* scratch = nullptr;
+  int compute_units = 256;  // of the handle's device, read at create
+  Layout lay{};             // offsets of the scratch parts
+  hipEvent_t done = nullptr;  // recorded after each call's last launch (destroy waits on it)
+};
+
+namespace {
 
 int check_limits(const ds_sel_limits* lim) {
   if (!lim || lim->struct_size != sizeof(ds_sel_limits)) return DS_SEL_E_INVALID;
@@ -207,22 +213,20 @@ int ds_sel_create(const ds_sel_limits* lim, ds_sel** out) {
       h->scratch = nullptr;
       return (int)DS_SEL_E_NOMEM;
     }
+    if (hipEventCreateWithFlags(&h->done, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(h->scratch);
+      h->scratch = nullptr;
+      h->done = nullptr;
+      return (int)DS_SEL_E_HIP;
+    }
     return (int)DS_SEL_OK;
   });
   if (rc != DS_SEL_OK) {
     delete h;
     return rc;
   }
-  h->scratch_bytes = s.total;
-  h->off_qt = s.qt;
-  h->off_qparts = s.qparts;
-  h->off_list = s.list;
-  h->off_counts = s.counts;
-  h->off_floor = s.floor;
-  h->off_ccount = s.ccount;
-  h->off_cand = s.cand;
-  h->off_part_ml = s.part_ml;
-  h->off_part_o = s.part_o;
+  h->lay = s;
   *out = h;
   return DS_SEL_OK;
 }
@@ -231,7 +235,12 @@ void ds_sel_destroy(ds_sel* h) {
   if (!h) return;
   if (h->scratch) {
     with_device(h->lim.device, [&]() {
-      (void)hipDeviceSynchronize();
+      // The handle's work ends with its last recorded event; wait for that
+      // only (hipFree itself does not wait for kernels still using the memory).
+      if (h->done) {
+        (void)hipEventSynchronize(h->done);
+        (void)hipEventDestroy(h->done);
+      }
       (void)hipFree(h->scratch);
       return (int)DS_SEL_OK;
     });
@@ -240,17 +249,94 @@ void ds_sel_destroy(ds_sel* h) {
 }
 
 namespace {
-int enqueue(ds_sel* h, const ds_sel_args* a, void* hip_stream, void* const* events);
+// Where one call's scratch lives: the handle's allocation, or the static array.
+struct Target {
+  int device;
+  int compute_units;
+  int32_t flags;
+  char* scratch;
+  Layout lay;
+  hipEvent_t done;  // the handle's completion event, or null
+};
+
+// Record the handle's completion event after a call's launches, unless the
+// stream is being captured into a graph (the event would then not mark this
+// call's completion).
+int mark_done(hipEvent_t done, hipStream_t stream) {
+  if (!done) return DS_SEL_OK;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return DS_SEL_OK;
+  }
+  if (st != hipStreamCaptureStatusNone) return DS_SEL_OK;
+  return hipEventRecord(done, stream) == hipSuccess ? DS_SEL_OK : DS_SEL_E_HIP;
+}
+int enqueue(const Target& t, const ds_sel_args* a, void* hip_stream, void* const* events);
+
+Target handle_target(const ds_sel* h) {
+  Target t;
+  t.device = h->lim.device;
+  t.compute_units = h->compute_units;
+  t.flags = h->lim.flags;
+  t.scratch = static_cast<char*>(h->scratch);
+  t.lay = h->lay;
+  t.done = h->done;
+  return t;
 }
 
+}  // namespace
+
 int ds_sel_score_select(ds_sel* h, const ds_sel_args* a, void* hip_stream) {
-  return enqueue(h, a, hip_stream, nullptr);
+  if (!h) return DS_SEL_E_INVALID;
+  const int rc = check_args(h->lim, a);
+  if (rc != DS_SEL_OK) return rc;
+  return enqueue(handle_target(h), a, hip_stream, nullptr);
 }
 
 int ds_sel_score_select_profiled(ds_sel* h, const ds_sel_args* a, void* hip_stream,
                                  void* const events[4]) {
   if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return DS_SEL_E_INVALID;
-  return enqueue(h, a, hip_stream, events);
+  if (!h) return DS_SEL_E_INVALID;
+  const int rc = check_args(h->lim, a);
+  if (rc != DS_SEL_OK) return rc;
+  return enqueue(handle_target(h), a, hip_stream, events);
+}
+
+int ds_sel_calibrate(const ds_sel_calib_args* a, void* hip_stream) {
+  if (!a || a->struct_size != sizeof(ds_sel_calib_args) || a->reserved != 0) return DS_SEL_E_INVALID;
+  if (a->workgroups < 1 || a->workgroups > 65535 || !a->sink) return DS_SEL_E_INVALID;
+  if (a->kind != DS_SEL_CALIB_EMPTY) {
+    if (a->layers < 1 || a->blocks < 1 || !a->keys || !aligned(a->keys, 16)) return DS_SEL_E_INVALID;
+    if (a->dim != 32 && a->dim != 64 && a->dim != 128 && a->dim != 256) return DS_SEL_E_INVALID;
+    if (a->ldk < a->dim || a->ldk % 8 != 0 || a->key_layer_stride % 8 != 0) return DS_SEL_E_INVALID;
+    if (a->layers > 1 && a->key_layer_stride < a->blocks * a->ldk) return DS_SEL_E_INVALID;
+  }
+  if (a->kind == DS_SEL_CALIB_READ) {
+    if (a->ldk != a->dim || (a->layers > 1 && a->key_layer_stride != a->blocks * a->dim))
+      return DS_SEL_E_INVALID;
+  } else if (a->kind == DS_SEL_CALIB_GATHER) {
+    if (!a->ranges || !aligned(a->ranges, 8) || !aligned(a->mask, 4)) return DS_SEL_E_INVALID;
+    if (a->mask && a->layers > 1 && a->mask_layer_stride < (a->blocks + 31) / 32) return DS_SEL_E_INVALID;
+  } else if (a->kind != DS_SEL_CALIB_EMPTY) {
+    return DS_SEL_E_INVALID;
+  }
+  dssel::CalibCall c{};
+  c.kind = a->kind;
+  c.workgroups = a->workgroups;
+  c.layers = a->layers;
+  c.dim = a->dim;
+  c.blocks = a->blocks;
+  c.ldk = a->ldk;
+  c.key_layer_stride = a->key_layer_stride;
+  c.mask_layer_stride = a->mask_layer_stride;
+  c.keys = static_cast<const uint16_t*>(a->keys);
+  c.mask = a->mask;
+  c.ranges = a->ranges;
+  c.sink = a->sink;
+  return dssel::launch_calibrate(c, static_cast<hipStream_t>(hip_stream)) == hipSuccess
+             ? (int)DS_SEL_OK
+             : (int)DS_SEL_E_HIP;
 }
 
 int ds_sel_check_attend_args(const ds_sel_limits* lim, const ds_sel_attend_args* a) {
@@ -299,22 +385,20 @@ int ds_sel_attend(ds_sel* h, const ds_sel_attend_args* a, void* hip_stream) {
   c.count = a->count;
   c.out = a->out;
   char* base = static_cast<char*>(h->scratch);
-  c.part_ml = reinterpret_cast<float*>(base + h->off_part_ml);
-  c.part_o = reinterpret_cast<float*>(base + h->off_part_o);
+  c.part_ml = reinterpret_cast<float*>(base + h->lay.part_ml);
+  c.part_o = reinterpret_cast<float*>(base + h->lay.part_o);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   return with_device(h->lim.device, [&]() {
-    return dssel::launch_attend(c, stream) == hipSuccess ? (int)DS_SEL_OK : (int)DS_SEL_E_HIP;
+    if (dssel::launch_attend(c, stream) != hipSuccess) return (int)DS_SEL_E_HIP;
+    return mark_done(h->done, stream);
   });
 }
 
 }  // extern "C"
 
 namespace {
-int enqueue(ds_sel* h, const ds_sel_args* a, void* hip_stream, void* const* events) {
-  if (!h) return DS_SEL_E_INVALID;
-  int rc = check_args(h->lim, a);
-  if (rc != DS_SEL_OK) return rc;
-
+// Enqueue the chain for an already validated call on the target's scratch.
+int enqueue(const Target& t, const ds_sel_args* a, void* hip_stream, void* const* events) {
   dssel::Call c{};
   c.layers = a->layers;
   c.rows = a->rows;
@@ -334,14 +418,14 @@ int enqueue(ds_sel* h, const ds_sel_args* a, void* hip_stream, void* const* even
   c.mode = !a->mask ? dssel::kNoMask
                     : ((a->mask_row_stride == 0 || a->rows == 1) ? dssel::kSharedMask
                                                                  : dssel::kRowMask);
-  c.engine = (h->lim.flags & DS_SEL_FLAG_VALU_SCORE) ? dssel::kEngineValu : dssel::kEngineMfma;
+  c.engine = (t.flags & DS_SEL_FLAG_VALU_SCORE) ? dssel::kEngineValu : dssel::kEngineMfma;
   c.ntiles = (int32_t)((a->blocks + dssel::kTileBlocks - 1) / dssel::kTileBlocks);
   c.cand_stride = (a->blocks + 3) / 4 * 4;
   {
     // Score grid: every resident slot (four workgroups per compute unit), and
     // enough workgroups that a piece never exceeds kScorePieceMax positions
     // even when every block is admitted.
-    const int64_t slots = (int64_t)dssel::kScoreWgsPerCu * h->compute_units;
+    const int64_t slots = (int64_t)dssel::kScoreWgsPerCu * t.compute_units;
     const int64_t need = a->layers + ((int64_t)a->layers * a->blocks + dssel::kScorePieceMax - 1) /
                                          dssel::kScorePieceMax;
     c.score_slots = (int32_t)slots;
@@ -350,25 +434,25 @@ int enqueue(ds_sel* h, const ds_sel_args* a, void* hip_stream, void* const* even
   c.out_idx = a->out_idx;
   c.out_score = a->out_score;
   c.out_count = a->out_count;
-  char* base = static_cast<char*>(h->scratch);
-  c.qt = reinterpret_cast<float*>(base + h->off_qt);
-  c.qparts = reinterpret_cast<uint16_t*>(base + h->off_qparts);
-  c.list = reinterpret_cast<int32_t*>(base + h->off_list);
-  c.counts = reinterpret_cast<int32_t*>(base + h->off_counts);
-  c.floor_key = reinterpret_cast<uint32_t*>(base + h->off_floor);
-  c.cand_count = reinterpret_cast<int32_t*>(base + h->off_ccount);
-  c.cand = reinterpret_cast<uint64_t*>(base + h->off_cand);
+  char* base = t.scratch;
+  c.qt = reinterpret_cast<float*>(base + t.lay.qt);
+  c.qparts = reinterpret_cast<uint16_t*>(base + t.lay.qparts);
+  c.list = reinterpret_cast<int32_t*>(base + t.lay.list);
+  c.counts = reinterpret_cast<int32_t*>(base + t.lay.counts);
+  c.floor_key = reinterpret_cast<uint32_t*>(base + t.lay.floor);
+  c.cand_count = reinterpret_cast<int32_t*>(base + t.lay.ccount);
+  c.cand = reinterpret_cast<uint64_t*>(base + t.lay.cand);
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   auto mark = [&](int i) {
     return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) == hipSuccess;
   };
-  return with_device(h->lim.device, [&]() {
+  return with_device(t.device, [&]() {
     if (!mark(0)) return (int)DS_SEL_E_HIP;
     if (dssel::launch_prep(c, stream) != hipSuccess || !mark(1)) return (int)DS_SEL_E_HIP;
     if (dssel::launch_score(c, stream) != hipSuccess || !mark(2)) return (int)DS_SEL_E_HIP;
     if (dssel::launch_select(c, stream) != hipSuccess || !mark(3)) return (int)DS_SEL_E_HIP;
-    return (int)DS_SEL_OK;
+    return mark_done(t.done, stream);
   });
 }
 }  // namespace

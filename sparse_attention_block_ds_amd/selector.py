@@ -26,7 +26,11 @@ DS_SEL_FLAG_VALU_SCORE = 1
 
 EXPORTED = ("ds_sel_create", "ds_sel_score_select", "ds_sel_score_select_profiled",
             "ds_sel_destroy", "ds_sel_check_args", "ds_sel_scratch_bytes", "ds_sel_status_string",
-            "ds_sel_attend", "ds_sel_check_attend_args")
+            "ds_sel_attend", "ds_sel_check_attend_args", "ds_sel_calibrate")
+
+DS_SEL_CALIB_EMPTY = 0
+DS_SEL_CALIB_READ = 1
+DS_SEL_CALIB_GATHER = 2
 
 
 class Limits(ctypes.Structure):
@@ -58,6 +62,16 @@ class AttendArgs(ctypes.Structure):
                 ("values", ctypes.c_void_p), ("ldv", ctypes.c_int64),
                 ("value_layer_stride", ctypes.c_int64), ("idx", ctypes.c_void_p),
                 ("count", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+
+
+class CalibArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("kind", ctypes.c_int32),
+                ("workgroups", ctypes.c_int32), ("layers", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("reserved", ctypes.c_int32), ("blocks", ctypes.c_int64),
+                ("keys", ctypes.c_void_p), ("ldk", ctypes.c_int64),
+                ("key_layer_stride", ctypes.c_int64), ("mask", ctypes.c_void_p),
+                ("mask_layer_stride", ctypes.c_int64), ("ranges", ctypes.c_void_p),
+                ("sink", ctypes.c_void_p)]
 
 
 class DsSelError(RuntimeError):
@@ -98,6 +112,8 @@ def load_library(path: Optional[str] = None):
     lib.ds_sel_attend.restype = ctypes.c_int
     lib.ds_sel_check_attend_args.argtypes = [P(Limits), P(AttendArgs)]
     lib.ds_sel_check_attend_args.restype = ctypes.c_int
+    lib.ds_sel_calibrate.argtypes = [P(CalibArgs), ctypes.c_void_p]
+    lib.ds_sel_calibrate.restype = ctypes.c_int
     lib.ds_sel_status_string.argtypes = [ctypes.c_int]
     lib.ds_sel_status_string.restype = ctypes.c_char_p
     if default:
@@ -144,11 +160,11 @@ def check_select_tensors(q, w, keys, k, mask=None, limit=None, out=None, device=
     _require(w.dtype == torch.bfloat16 and tuple(w.shape) == (L, R, H) and w.is_contiguous(),
              "w must be a contiguous bf16 tensor [L, R, H]")
     _require(keys.dtype == torch.bfloat16 and keys.dim() == 3 and keys.shape[0] == L and
-             keys.shape[2] >= d and keys.stride(2) == 1,
-             "keys must be a bf16 tensor [L, N, ldk] with ldk >= d and unit stride in the last dim")
-    if keys.shape[1] > 1:
-        _require(keys.stride(1) >= d, "keys rows overlap (stride(1) < d)")
+             keys.shape[2] >= d, "keys must be a bf16 tensor [L, N, ldk] with ldk >= d")
     N = keys.shape[1]
+    if N > 0:  # an empty key tensor is never read, whatever its strides
+        _require(keys.stride(2) == 1, "keys must have unit stride in the last dim")
+        _require(N == 1 or keys.stride(1) >= d, "keys rows overlap (stride(1) < d)")
     tensors = [(q, "q"), (w, "w"), (keys, "keys")]
     if mask is not None:
         _require(mask.dtype == torch.int32 and mask.dim() == 3 and mask.shape[0] == L and
@@ -190,7 +206,7 @@ def check_attend_tensors(qa, keys, values, idx, count, scale, out=None, device=N
     L, R, Ha, d = qa.shape
     for t, name in ((keys, "keys"), (values, "values")):
         _require(t.dtype == torch.bfloat16 and t.dim() == 3 and t.shape[0] == L and
-                 t.shape[2] >= d and t.stride(2) == 1,
+                 t.shape[2] >= d and (t.shape[1] == 0 or t.stride(2) == 1),
                  f"{name} must be a bf16 tensor [L, N, ld] with ld >= d and unit stride in the last dim")
     _require(keys.shape[1] == values.shape[1], "keys and values must hold the same number of blocks")
     _require(idx.dtype == torch.int32 and idx.dim() == 3 and tuple(idx.shape[:2]) == (L, R) and
@@ -351,3 +367,27 @@ def upload(problem, device="cuda"):
     if problem.limit is not None:
         limit = torch.from_numpy(np.ascontiguousarray(problem.limit, dtype=np.int32)).to(device)
     return q, w, keys, mask, limit
+
+
+def calibrate(kind, workgroups, sink, keys=None, mask=None, ranges=None, stream=None):
+    """Enqueue one calibration launch (ds_sel_calibrate) on `stream` (default:
+    torch's current stream).  keys bf16 [L,N,ldk]; mask int32 [L,1,words] or
+    None; ranges int64 [workgroups + 1] (gather); sink int32 [>= workgroups]."""
+    import torch
+    lib = load_library()
+    a = CalibArgs()
+    a.struct_size = ctypes.sizeof(CalibArgs)
+    a.kind, a.workgroups, a.reserved = kind, workgroups, 0
+    if keys is not None:
+        a.layers, a.blocks, a.dim = keys.shape[0], keys.shape[1], keys.shape[2]
+        a.keys, a.ldk, a.key_layer_stride = _ptr(keys), keys.stride(1), keys.stride(0)
+    if mask is not None:
+        a.mask, a.mask_layer_stride = _ptr(mask), mask.stride(0)
+    a.ranges, a.sink = _ptr(ranges), _ptr(sink)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    rc = lib.ds_sel_calibrate(ctypes.byref(a), ctypes.c_void_p(handle))
+    if rc != DS_SEL_OK:
+        raise DsSelError(rc, "ds_sel_calibrate")
+

@@ -25,6 +25,7 @@ tiny       1   1  4   64   4096    q, K, w integers uniform in [-3, 3]; limit = 
                                    Bernoulli(0.6) mask AND limit = N
 verify     1   6  64  128  32768   as 8k per row; limit_r = N - 5 + r; no mask
 verify_int 1   6  64  128  32768   q, K, w integers in [-3, 3]; limit_r = N - 5 + r
+300k_x43   43  1  64  128  75000   43 independent layers, each drawn like 300k
 sweep      43  6  64  128  75000   K, q in {-1,0,1}, w in {0,1}; layer l has one mask shared
                                    by its rows, Bernoulli(p_l), p_l = 0.1 + 0.9 l / 42;
                                    limit_r = N - 5 + r
@@ -162,6 +163,24 @@ def make(name: str, **overrides) -> Problem:
         mask = pack_mask((rng.random(N) < 0.6)[None, None, :])
         return Problem("300k", 512, q, w, keys, mask, np.full((L, R), N, np.int32), False,
                        {"seed": 2, "heavy": heavy.size, "p": 0.6})
+    if name == "300k_x43":
+        # 43 distinct 300k problems (one row each) in one call: the batched form
+        # of the 300k config.  Each layer is drawn like the 300k config, all from
+        # one generator: q, w, then per layer K, its heavy set and its mask.
+        rng = np.random.default_rng(overrides.get("seed", 2))
+        L = overrides.get("layers", 43)
+        R, H, d, N = 1, 64, 128, overrides.get("blocks", 75000)
+        q = _normal_bits(rng, (L, R, H, d))
+        w = _uniform01_bits(rng, (L, R, H))
+        keys = np.empty((L, N, d), np.uint16)
+        bits = np.empty((L, 1, N), bool)
+        for l in range(L):
+            kf = bf16_bits_to_f32(_normal_bits(rng, (N, d)))
+            kf[rng.choice(N, size=int(0.05 * N), replace=False), :] *= 4.0
+            keys[l] = f32_to_bf16_bits(kf)
+            bits[l, 0] = rng.random(N) < 0.6
+        return Problem("300k_x43", 512, q, w, keys, pack_mask(bits), np.full((L, R), N, np.int32),
+                       False, {"seed": 2, "p": 0.6})
     if name in ("verify", "verify_int"):
         rng = np.random.default_rng(overrides.get("seed", 3))
         L, R, H, d, N = 1, 6, 64, 128, 32768

@@ -272,3 +272,4 @@ def test_attend_capacity_enforced(lib, field, value):
     a = _attend_args(L=1)
     setattr(a, field, value)
     assert check_attend(lib, a) == sel.DS_SEL_E_CAPACITY
+

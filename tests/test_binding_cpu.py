@@ -120,3 +120,30 @@ def test_attend_accepts_well_formed():
 def test_attend_rejects(name, value):
     with pytest.raises(ValueError):
         check_attend(**{name: value})
+
+
+def _gpu_test_problems():
+    """Every problem shape the GPU parity tests feed through the binding."""
+    import numpy as np
+    from sparse_attention_block_ds_amd import workloads as wl
+    from tests import test_gpu_parity as tg
+    probs = [wl.make_custom(*c["args"], seed=100 + i, **c["kw"]) for i, c in enumerate(tg.EDGE)]
+    probs += [wl.make(n) for n in ("tiny", "8k", "verify")]
+    probs.append(wl.make_custom(43, 8, 8, 64, 3000, 512, seed=1, values="int3", mask_p=0.7))
+    probs.append(wl.make_custom(3, 6, 64, 128, 1200, 512, seed=2, values="normal", mask_p=0.5,
+                                mask_shared=False, limits=np.array([[1200 - 5 + r for r in range(6)]])))
+    return probs
+
+
+def test_accepts_every_gpu_test_shape():
+    """The shapes the GPU tests use (empty N, padded rows, per-row masks, ...) pass
+    the binding's checks as uploaded, so a GPU run is never spent on a check."""
+    for p in _gpu_test_problems():
+        q, w, keys, mask, limit = sel.upload(p, "cpu")
+        sel.check_select_tensors(q, w, keys, p.k, mask, limit, None, CPU)
+        out = (torch.empty(p.layers, p.rows, p.k, dtype=torch.int32), torch.empty(p.layers, p.rows, p.k),
+               torch.empty(p.layers, p.rows, dtype=torch.int32))
+        sel.check_select_tensors(q, w, keys, p.k, mask, limit, out, CPU)
+        qa = torch.zeros(p.layers, p.rows, 2, p.dim, dtype=BF)
+        idx = torch.zeros(p.layers, p.rows, p.k, dtype=torch.int32)
+        sel.check_attend_tensors(qa, keys, keys, idx, None, 0.5, None, CPU)
