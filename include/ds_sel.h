@@ -145,6 +145,26 @@ int ds_sel_score_select(ds_sel* h, const ds_sel_args* a, void* hip_stream);
 int ds_sel_score_select_profiled(ds_sel* h, const ds_sel_args* a, void* hip_stream,
                                  void* const events[4]);
 
+/* The same selection as ds_sel_score_select, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  No handle is needed and nothing is
+ * allocated: the chain's scratch is a static device array of 64 MiB inside the
+ * library, one per GPU, held until the process ends.  `device` is the HIP
+ * ordinal the pointers in `a` live on; `flags` takes DS_SEL_FLAG_* as
+ * ds_sel_limits.flags does.  The arguments are checked as for
+ * ds_sel_score_select against this build's hard limits; a call whose scratch
+ * (ds_sel_noalloc_scratch_bytes) exceeds 64 MiB returns DS_SEL_E_CAPACITY and
+ * enqueues nothing.  Every call on one GPU uses that GPU's one array, so calls
+ * that overlap in time on one GPU (different streams, or different host
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.  DS_SEL_E_NODEVICE when `device` does not exist. */
+int ds_sel_score_select_noalloc(int32_t device, uint32_t flags, const ds_sel_args* a,
+                                void* hip_stream);
+
+/* Bytes of the static scratch ds_sel_score_select_noalloc needs for the call
+ * `a` (-1 when a's sizes are invalid). */
+int64_t ds_sel_noalloc_scratch_bytes(const ds_sel_args* a);
+
 /* Attention over a selection -- the step that consumes it (page "DeepSeek
  * V4.1F Q4 on M3 Ultra with native DSpark MTP (40tps / 800tps)", paragraph
  * "Decode at depth": each layer's compressed attention works on the blocks

@@ -285,6 +285,46 @@ Target handle_target(const ds_sel* h) {
   return t;
 }
 
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing: its scratch is this file-scope
+// device array (one copy per GPU, held until the process ends).  Host code
+// never passes the array's name to a kernel or a copy: the name is a host-side
+// stand-in, so the array's device address is looked up once per device with
+// hipGetSymbolAddress and that pointer is used instead.
+constexpr int64_t kStaticScratchBytes = 64ll << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct StaticSlot {
+  bool ready = false;
+  void* ptr = nullptr;
+  int compute_units = 256;
+};
+StaticSlot g_static[kMaxDevices];
+std::mutex g_static_mu;
+
+// The array's address and the compute-unit count on `device` (made current by
+// the caller), looked up on the first call on that device.
+int static_slot(int device, StaticSlot* out) {
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticSlot& s = g_static[device];
+  if (!s.ready) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return DS_SEL_E_HIP;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
+        cus > 0)
+      s.compute_units = cus;
+    (void)hipGetLastError();
+    s.ptr = ptr;
+    s.ready = true;
+  }
+  *out = s;
+  return DS_SEL_OK;
+}
 }  // namespace
 
 int ds_sel_score_select(ds_sel* h, const ds_sel_args* a, void* hip_stream) {
@@ -301,6 +341,64 @@ int ds_sel_score_select_profiled(ds_sel* h, const ds_sel_args* a, void* hip_stre
   const int rc = check_args(h->lim, a);
   if (rc != DS_SEL_OK) return rc;
   return enqueue(handle_target(h), a, hip_stream, events);
+}
+
+int64_t ds_sel_noalloc_scratch_bytes(const ds_sel_args* a) {
+  if (!a || a->struct_size != sizeof(ds_sel_args) || a->layers < 1 || a->rows < 1 || a->dim < 1 ||
+      a->blocks < 0 || a->rows > DS_SEL_MAX_ROWS || a->dim > DS_SEL_MAX_DIM ||
+      a->blocks > DS_SEL_MAX_BLOCKS)
+    return -1;
+  ds_sel_limits lim{};
+  lim.struct_size = sizeof(ds_sel_limits);
+  lim.max_layers = a->layers;
+  lim.max_rows = a->rows;
+  lim.max_dim = a->dim;
+  lim.max_blocks = a->blocks;
+  return layout_for(lim, false).total;
+}
+
+int ds_sel_score_select_noalloc(int32_t device, uint32_t flags, const ds_sel_args* a,
+                                void* hip_stream) {
+  if (device < 0 || device >= kMaxDevices || (flags & ~DS_SEL_FLAG_VALU_SCORE) != 0)
+    return DS_SEL_E_INVALID;
+  // Checks against the build's hard limits only; the static array decides the rest.
+  ds_sel_limits lim{};
+  lim.struct_size = sizeof(ds_sel_limits);
+  lim.device = device;
+  lim.max_layers = 65535;
+  lim.max_rows = DS_SEL_MAX_ROWS;
+  lim.max_heads = DS_SEL_MAX_HEADS;
+  lim.max_dim = DS_SEL_MAX_DIM;
+  lim.max_k = DS_SEL_MAX_K;
+  lim.max_blocks = DS_SEL_MAX_BLOCKS;
+  lim.flags = (int32_t)flags;
+  int rc = check_args(lim, a);
+  if (rc != DS_SEL_OK) return rc;
+  const int64_t need = ds_sel_noalloc_scratch_bytes(a);
+  if (need < 0 || need > kStaticScratchBytes) return DS_SEL_E_CAPACITY;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0 || device >= ndev) {
+    (void)hipGetLastError();
+    return DS_SEL_E_NODEVICE;
+  }
+  return with_device(device, [&]() {
+    StaticSlot slot;
+    const int src = static_slot(device, &slot);
+    if (src != DS_SEL_OK) return src;
+    ds_sel_limits call_lim = lim;
+    call_lim.max_layers = a->layers;
+    call_lim.max_rows = a->rows;
+    call_lim.max_dim = a->dim;
+    call_lim.max_blocks = a->blocks;
+    Target t;
+    t.device = device;
+    t.compute_units = slot.compute_units;
+    t.flags = (int32_t)flags;
+    t.scratch = static_cast<char*>(slot.ptr);
+    t.lay = layout_for(call_lim, false);
+    t.done = nullptr;
+    return enqueue(t, a, hip_stream, nullptr);
+  });
 }
 
 int ds_sel_calibrate(const ds_sel_calib_args* a, void* hip_stream) {

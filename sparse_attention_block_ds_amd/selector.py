@@ -26,7 +26,8 @@ DS_SEL_FLAG_VALU_SCORE = 1
 
 EXPORTED = ("ds_sel_create", "ds_sel_score_select", "ds_sel_score_select_profiled",
             "ds_sel_destroy", "ds_sel_check_args", "ds_sel_scratch_bytes", "ds_sel_status_string",
-            "ds_sel_attend", "ds_sel_check_attend_args", "ds_sel_calibrate")
+            "ds_sel_attend", "ds_sel_check_attend_args", "ds_sel_calibrate",
+            "ds_sel_score_select_noalloc", "ds_sel_noalloc_scratch_bytes")
 
 DS_SEL_CALIB_EMPTY = 0
 DS_SEL_CALIB_READ = 1
@@ -112,6 +113,11 @@ def load_library(path: Optional[str] = None):
     lib.ds_sel_attend.restype = ctypes.c_int
     lib.ds_sel_check_attend_args.argtypes = [P(Limits), P(AttendArgs)]
     lib.ds_sel_check_attend_args.restype = ctypes.c_int
+    lib.ds_sel_score_select_noalloc.argtypes = [ctypes.c_int32, ctypes.c_uint32, P(Args),
+                                                ctypes.c_void_p]
+    lib.ds_sel_score_select_noalloc.restype = ctypes.c_int
+    lib.ds_sel_noalloc_scratch_bytes.argtypes = [P(Args)]
+    lib.ds_sel_noalloc_scratch_bytes.restype = ctypes.c_int64
     lib.ds_sel_calibrate.argtypes = [P(CalibArgs), ctypes.c_void_p]
     lib.ds_sel_calibrate.restype = ctypes.c_int
     lib.ds_sel_status_string.argtypes = [ctypes.c_int]
@@ -391,3 +397,25 @@ def calibrate(kind, workgroups, sink, keys=None, mask=None, ranges=None, stream=
     if rc != DS_SEL_OK:
         raise DsSelError(rc, "ds_sel_calibrate")
 
+
+def score_select_noalloc(q, w, keys, k, mask, limit, out, device=None, engine="mfma", stream=None):
+    """ds_sel_score_select_noalloc: the selection on the library's static
+    scratch, with caller-provided outputs (idx, score, count) and no handle.
+    Calls overlapping in time on one GPU race (they share the scratch)."""
+    import torch
+    if engine not in ("mfma", "valu"):
+        raise ValueError("engine must be 'mfma' or 'valu'")
+    if out is None:
+        raise ValueError("out (idx, score, count) is required: this entry point allocates nothing")
+    dev = q.device if device is None else torch.device("cuda", device)
+    check_select_tensors(q, w, keys, k, mask, limit, out, dev)
+    lib = load_library()
+    a = make_args(q, w, keys, k, mask, limit, *out)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    rc = lib.ds_sel_score_select_noalloc(dev.index, DS_SEL_FLAG_VALU_SCORE if engine == "valu" else 0,
+                                         ctypes.byref(a), ctypes.c_void_p(handle))
+    if rc != DS_SEL_OK:
+        raise DsSelError(rc, "ds_sel_score_select_noalloc")
+    return out

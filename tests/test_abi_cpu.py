@@ -273,3 +273,24 @@ def test_attend_capacity_enforced(lib, field, value):
     setattr(a, field, value)
     assert check_attend(lib, a) == sel.DS_SEL_E_CAPACITY
 
+
+def test_noalloc_checks_before_touching_a_device(lib):
+    """The static-scratch entry point validates and sizes the call on the host:
+    oversize calls are refused with CAPACITY, bad ones with INVALID, and only a
+    well-formed call reaches the device lookup (NODEVICE here)."""
+    def args(L, R, d, N, k=16):
+        a = sel.Args()
+        a.struct_size = ctypes.sizeof(sel.Args)
+        a.layers, a.rows, a.heads, a.dim, a.k, a.blocks = L, R, 4, d, k, N
+        a.q = a.w = a.keys = a.out_idx = a.out_score = ctypes.c_void_p(256)
+        a.ldk, a.key_layer_stride = d, N * d
+        return a
+    small, big = args(1, 6, 128, 32768), args(1, 8, 128, 1 << 22)
+    assert 0 < lib.ds_sel_noalloc_scratch_bytes(ctypes.byref(small)) <= 64 << 20
+    assert lib.ds_sel_noalloc_scratch_bytes(ctypes.byref(big)) > 64 << 20
+    assert lib.ds_sel_score_select_noalloc(0, 0, ctypes.byref(big), None) == sel.DS_SEL_E_CAPACITY
+    bad = args(1, 6, 128, 32768, k=0)
+    assert lib.ds_sel_score_select_noalloc(0, 0, ctypes.byref(bad), None) == sel.DS_SEL_E_INVALID
+    assert lib.ds_sel_score_select_noalloc(0, 4, ctypes.byref(small), None) == sel.DS_SEL_E_INVALID
+    assert lib.ds_sel_score_select_noalloc(-1, 0, ctypes.byref(small), None) == sel.DS_SEL_E_INVALID
+    assert lib.ds_sel_score_select_noalloc(0, 0, ctypes.byref(small), None) == sel.DS_SEL_E_NODEVICE
