@@ -79,69 +79,6 @@ struct Call {
   uint64_t* cand;      // [L][R][cand_stride] (key << 32) | ~position, unordered
 };
 
-// ------------------------------------------------------------------ chain
-// The whole selection in one launch.  Workgroups claim tickets in order from
-// a counter; the tickets name tasks, and a task waits only for tasks with
-// lower tickets, which are held by workgroups already running, so every wait
-// ends whatever the number of resident workgroups.  Ticket order:
-//   L R fold tasks (one per (layer, row)), 4 L sample tasks (one per
-//   (layer, quarter of the sample slots)), then for each layer l the C chunk
-//   tasks of layer l followed by the R select tasks of layer l - 1, and last
-//   the R select tasks of layer L - 1.
-constexpr int kChainThreads = 256;      // 4 waves
-constexpr int kChainWgsPerCu = 4;       // resident chain workgroups per compute unit
-constexpr int kSampleTasks = 4;         // sample tasks per layer, 128 slots each
-constexpr int kChunkMin = 64;           // blocks per chunk: at least,
-constexpr int kChunkMax = 2048;         // and at most (one mask word per lane of a wave)
-constexpr int kPrefixMax = 4096;        // chunks per layer the select indexes in LDS
-constexpr int kSelectRegs = 4096;       // candidates the select holds in registers
-
-// Synchronisation words (uint32), each counter on its own 128-byte line.
-constexpr int kSyncLine = 32;
-constexpr int kSyncTicket = 0, kSyncExit = kSyncLine, kSyncError = 2 * kSyncLine;
-constexpr int kSyncGlobalWords = 3 * kSyncLine;
-constexpr int kSyncLayerWords = 4 * kSyncLine;
-// within a layer's record
-constexpr int kSyncFold = 0, kSyncSample = 1;          // line 0: fold and sample tasks done
-constexpr int kSyncFloor = kSyncLine;                   // line 1: floors ready (0 / 1)
-constexpr int kSyncChunk = 2 * kSyncLine;               // line 2: chunk tasks done
-constexpr int kSyncSelect = 3 * kSyncLine;              // line 3: select tasks done,
-constexpr int kSyncCount = 3 * kSyncLine + 8;           //   then the admitted count per row
-
-// Device error bits (the word at kSyncError): a wait gave up.
-constexpr uint32_t kErrFoldWait = 1u, kErrFloorWait = 2u, kErrChunkWait = 4u;
-constexpr uint32_t kSpinLimit = 1u << 22;
-
-struct ChainCall {
-  int32_t layers, rows, heads, dim, k;
-  int32_t mode, engine;
-  int32_t chunk;        // T: blocks per chunk, a multiple of 64 in [kChunkMin, kChunkMax]
-  int32_t chunks;       // C = ceil(N / T) per layer
-  int32_t tickets;      // L R + kSampleTasks L + L C + L R
-  int64_t blocks;
-  int64_t cand_stride;  // C T: candidate slots per (layer, row); chunk c owns [c T, c T + T)
-  const uint16_t* q;
-  const uint16_t* w;
-  const uint16_t* keys;
-  int64_t ldk, key_layer_stride;
-  const uint32_t* mask;
-  int64_t mask_row_stride, mask_layer_stride;
-  const int32_t* limit;
-  int32_t* out_idx;
-  float* out_score;
-  int32_t* out_count;
-  // scratch
-  uint32_t* sync;      // kSyncGlobalWords + L kSyncLayerWords, zero between calls
-  float* qt;           // [L][R][d] folded query rows, fp32
-  uint16_t* qparts;    // [L][3][R][d] bf16 parts of q~: hi = bf16(q~), mid, lo
-  uint32_t* skey;      // [L][R][kSampleSlots] sampled keys (0: not admitted by the row)
-  uint32_t* floor_key; // [L][R] candidate floors
-  int32_t* ccount;     // [L][R][C] candidates per chunk
-  uint64_t* cand;      // [L][R][C T] (key << 32) | ~block, chunk c's run at c T
-};
-
-hipError_t launch_chain(const ChainCall& c, int workgroups, hipStream_t stream);
-
 // Attention over the selected blocks.  One workgroup of kAttendThreads per
 // (head tile, split, row, layer); a split covers chunks_per_split chunks of
 // kAttendChunk selected blocks.  With several splits each writes a partial
