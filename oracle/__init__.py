@@ -13,6 +13,10 @@ whole context, only mask-admitted blocks are candidates, the admitted index is
 built per row, the top 512 are kept).  The score formula, the order and the
 padding are readings of this library, stated in the C file's header.
 
+``quantize_q8`` / ``select_q8`` / ``score_blocks_q8`` are the 8-bit key
+stream: keys stored as groups of 32 signed 8-bit codes with one fp16 scale,
+scored on their dequantised values (the C file states the reading).
+
 ``attend`` is the step after the selection, read the same way: per attention
 head, the softmax over the selected blocks of scale * (q . K[b]) applied to the
 blocks' values V[b], in double precision (the C file states the reading).
@@ -55,6 +59,14 @@ def _declare(lib):
     lib.ds_sel_oracle_score_blocks.argtypes = [i32, i32, i32, i32, i64, p, p, p, i64, i64, i32,
                                                i32, i64, p, p]
     lib.ds_sel_oracle_attend.restype = ctypes.c_int
+    lib.ds_sel_oracle_quantize_q8.restype = ctypes.c_int
+    lib.ds_sel_oracle_quantize_q8.argtypes = [i32, i64, i32, p, i64, i64, p, i64, i64, p, i64, i64]
+    lib.ds_sel_oracle_select_q8.restype = ctypes.c_int
+    lib.ds_sel_oracle_select_q8.argtypes = [i32, i32, i32, i32, i64, i32, p, p, p, i64, i64, p, i64,
+                                            i64, p, i64, i64, p, p, p, p]
+    lib.ds_sel_oracle_score_blocks_q8.restype = ctypes.c_int
+    lib.ds_sel_oracle_score_blocks_q8.argtypes = [i32, i32, i32, i32, i64, p, p, p, i64, i64, p, i64,
+                                                  i64, i32, i32, i64, p, p]
     lib.ds_sel_oracle_attend.argtypes = [i32, i32, i32, i32, i64, i32, p, p, i64, i64, p, i64, i64,
                                          p, p, ctypes.c_double, p]
     return lib
@@ -144,6 +156,74 @@ def score_blocks(q, w, keys, layer, row, blocks_list, lib=None):
                                         _ptr(lst), _ptr(out))
     if rc != 0:
         raise OracleError(f"ds_sel_oracle_score_blocks returned {rc}")
+    return out
+
+
+def quantize_q8(keys, lib=None):
+    """The 8-bit key stream of bf16 keys [L][N][ldk] (columns past d = ldk are
+    all used: pass exactly [L][N][d]).  Returns (codes int8 [L][N][d], scales
+    uint16 fp16 bits [L][N][d/32])."""
+    keys = _c(keys, np.uint16)
+    L, N, d = keys.shape
+    codes = np.empty((L, N, d), np.int8)
+    scales = np.empty((L, N, d // 32), np.uint16)
+    lib = lib or load()
+    rc = lib.ds_sel_oracle_quantize_q8(L, N, d, _ptr(keys), d, N * d, _ptr(codes), d, N * d,
+                                       _ptr(scales), d // 32, N * (d // 32))
+    if rc != 0:
+        raise OracleError(f"ds_sel_oracle_quantize_q8 returned {rc}")
+    return codes, scales
+
+
+def _q8_shapes(q, codes, scales):
+    layers, rows, heads, dim = q.shape
+    if codes.ndim != 3 or codes.shape[0] != layers or codes.shape[2] != dim:
+        raise ValueError("codes must be [layers][blocks][dim]")
+    if scales.shape != (layers, codes.shape[1], dim // 32):
+        raise ValueError("scales must be [layers][blocks][dim/32]")
+    return codes.shape[1]
+
+
+def select_q8(q, w, codes, scales, k, mask=None, limit=None, lib=None):
+    """Top-k selection on the 8-bit key stream (codes int8 [L][N][d], scales
+    fp16 bits [L][N][d/32]); otherwise as select()."""
+    q, w = _c(q, np.uint16), _c(w, np.uint16)
+    codes, scales = _c(codes, np.int8), _c(scales, np.uint16)
+    mask, limit = _c(mask, np.uint32), _c(limit, np.int32)
+    layers, rows, heads, dim = q.shape
+    blocks = _q8_shapes(q, codes, scales)
+    mrow = mlayer = 0
+    if mask is not None:
+        mrow = 0 if mask.shape[1] == 1 else mask.shape[2]
+        mlayer = mask.shape[1] * mask.shape[2]
+    idx = np.empty((layers, rows, k), np.int32)
+    score = np.empty((layers, rows, k), np.float32)
+    count = np.empty((layers, rows), np.int32)
+    lib = lib or load()
+    rc = lib.ds_sel_oracle_select_q8(layers, rows, heads, dim, blocks, k, _ptr(q), _ptr(w), _ptr(codes),
+                                     dim, blocks * dim, _ptr(scales), dim // 32, blocks * (dim // 32),
+                                     _ptr(mask), mrow, mlayer, _ptr(limit), _ptr(idx), _ptr(score),
+                                     _ptr(count))
+    if rc != 0:
+        raise OracleError(f"ds_sel_oracle_select_q8 returned {rc}")
+    return idx, score, count
+
+
+def score_blocks_q8(q, w, codes, scales, layer, row, blocks_list, lib=None):
+    """q8 scores (the oracle's fixed order) of the listed blocks of one (layer, row)."""
+    q, w = _c(q, np.uint16), _c(w, np.uint16)
+    codes, scales = _c(codes, np.int8), _c(scales, np.uint16)
+    lst = _c(blocks_list, np.int32)
+    layers, rows, heads, dim = q.shape
+    blocks = _q8_shapes(q, codes, scales)
+    out = np.empty(lst.shape[0], np.float32)
+    lib = lib or load()
+    rc = lib.ds_sel_oracle_score_blocks_q8(layers, rows, heads, dim, blocks, _ptr(q), _ptr(w),
+                                           _ptr(codes), dim, blocks * dim, _ptr(scales), dim // 32,
+                                           blocks * (dim // 32), layer, row, lst.shape[0], _ptr(lst),
+                                           _ptr(out))
+    if rc != 0:
+        raise OracleError(f"ds_sel_oracle_score_blocks_q8 returned {rc}")
     return out
 
 

@@ -273,6 +273,97 @@ def check_score_blocks(lib):
                                                   err_msg=f"score_blocks exact l={l} r={r}")
 
 
+# ------------------------------------------------------------------ 8-bit key stream
+def _half_rne_bits(x):
+    """fp32 -> fp16 bits by numpy's own conversion (round to nearest even)."""
+    return np.asarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
+def check_quantize_q8(lib):
+    """The quantiser against facts independent of its code: numpy's fp16
+    rounding of amax / 127, exact round trips, the rounding rule at ties, the
+    error bound |x - s c| <= s / 2, |c| <= 127, zero groups."""
+    rng = np.random.default_rng(60)
+    L, N, d = 2, 300, 128
+    x = rng.standard_normal((L, N, d)).astype(np.float32) * np.exp(rng.uniform(-6, 6, (L, N, 1))).astype(np.float32)
+    x[0, 7, 32:64] = 0.0                                    # an all-zero group
+    bits = wl.f32_to_bf16_bits(x)
+    codes, scales = oracle.quantize_q8(bits, lib=lib)
+    xf = wl.bf16_bits_to_f32(bits).reshape(L, N, d // 32, 32)
+    amax = np.abs(xf).max(axis=-1)
+    want = np.where(amax == 0, 0, _half_rne_bits(amax / np.float32(127)))
+    np.testing.assert_array_equal(scales, want.astype(np.uint16), err_msg="scale = fp16(amax / 127)")
+    s = scales.view(np.float16).astype(np.float64)[..., None]
+    c = codes.reshape(L, N, d // 32, 32).astype(np.float64)
+    assert np.all(np.abs(c) <= 127)
+    assert np.all(c[0, 7, 1] == 0) and s[0, 7, 1, 0] == 0
+    err = np.abs(xf.astype(np.float64) - s * c)
+    assert np.all(err <= s / 2 * (1 + 2 ** -20)), float(np.max(err / np.maximum(s, 1e-300)))
+    # the largest |x| of every non-zero group lands on |code| 126 or 127
+    top = np.take_along_axis(np.abs(c), np.abs(xf).argmax(axis=-1)[..., None], -1)[..., 0]
+    assert np.all(top[amax > 0] >= 126)
+    # exact round trip: codes times a power-of-two scale, with one |code| = 127
+    cc = rng.integers(-127, 128, (1, 64, d)).astype(np.float32)
+    cc[:, :, ::32] = 127
+    p2 = np.float32(2.0) ** rng.integers(-8, 8, (1, 64, 1)).astype(np.float32)
+    codes2, scales2 = oracle.quantize_q8(wl.f32_to_bf16_bits(cc * p2), lib=lib)
+    np.testing.assert_array_equal(codes2, cc.astype(np.int8), err_msg="round trip")
+    np.testing.assert_array_equal(scales2.view(np.float16).astype(np.float32),
+                                  np.broadcast_to(p2, (1, 64, d // 32)))
+    # ties: x / s = +-2.5 and +-0.5 round away from zero
+    g = np.zeros((1, 1, 32), np.float32)
+    g[0, 0, 0], g[0, 0, 1], g[0, 0, 2], g[0, 0, 3], g[0, 0, 4] = 127, 2.5, -2.5, 0.5, -0.5
+    codes3, _ = oracle.quantize_q8(wl.f32_to_bf16_bits(g), lib=lib)
+    assert list(codes3[0, 0, :5]) == [127, 3, -3, 1, -1], codes3[0, 0, :5]
+
+
+def _q8_problem(seed, L, R, H, d, N, k, pow2_scales, values="normal", **kw):
+    """A workload whose keys are replaced by an 8-bit stream: random codes in
+    [-127, 127] and scales either powers of two (dequantised keys exact in bf16)
+    or general fp16 values."""
+    p = wl.make_custom(L, R, H, d, N, k, seed=seed, values=values, **kw)
+    rng = np.random.default_rng(seed + 1)
+    codes = rng.integers(-127, 128, (L, N, d)).astype(np.int8)
+    if pow2_scales:
+        sc = (np.float32(2.0) ** rng.integers(-10, 3, (L, N, d // 32))).astype(np.float16)
+    else:
+        sc = rng.uniform(1e-3, 0.05, (L, N, d // 32)).astype(np.float16)
+    return p, codes, sc.view(np.uint16)
+
+
+def check_select_q8(lib):
+    """Selection on the 8-bit stream: identical bit for bit to the bf16 oracle
+    on the dequantised keys when those are exact in bf16; within the fp32
+    bound of fp64 otherwise; per-block scores equal the selection's."""
+    for kw in (dict(mask_p=0.6), dict(mask_p=0.4, mask_shared=False, limits=np.array([[299, 150, 7]]))):
+        p, codes, scales = _q8_problem(70, 1, 3, 8, 64, 300, 40, True, **kw)
+        deq = codes.astype(np.float32) * np.repeat(scales.view(np.float16).astype(np.float32), 32, axis=-1)
+        kb = wl.f32_to_bf16_bits(deq)
+        assert np.array_equal(wl.bf16_bits_to_f32(kb), deq), "dequantised keys must be bf16-exact here"
+        a = oracle.select_q8(p.q, p.w, codes, scales, p.k, p.mask, p.limit, lib=lib)
+        b = oracle.select(p.q, p.w, kb, p.k, p.mask, p.limit, lib=lib)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+    # general fp16 scales: every admitted score within 2 gamma_(d+H) of fp64
+    p, codes, scales = _q8_problem(71, 2, 2, 16, 128, 400, 400, False, mask_p=0.7)
+    idx, sc, cnt = oracle.select_q8(p.q, p.w, codes, scales, p.blocks, p.mask, p.limit, lib=lib)
+    q = wl.bf16_bits_to_f32(p.q).astype(np.float64)
+    w = wl.bf16_bits_to_f32(p.w).astype(np.float64)
+    deq = codes.astype(np.float64) * np.repeat(scales.view(np.float16).astype(np.float64), 32, axis=-1)
+    adm = admitted_mask(p)
+    for l in range(2):
+        for r in range(2):
+            n = int(cnt[l, r])
+            assert n == adm[l, r].sum()
+            blk = idx[l, r, :n]
+            s64 = w[l, r] @ (q[l, r] @ deq[l][blk].T)
+            mag = np.abs(w[l, r]) @ (np.abs(q[l, r]) @ np.abs(deq[l][blk]).T)
+            assert np.all(np.abs(sc[l, r, :n] - s64) <= 2 * gamma(128 + 16) * mag + 1e-30)
+            got = oracle.score_blocks_q8(p.q, p.w, codes, scales, l, r, np.sort(blk), lib=lib)
+            by = dict(zip(blk.tolist(), sc[l, r, :n].tolist()))
+            np.testing.assert_array_equal(got, np.array([by[b] for b in np.sort(blk).tolist()], np.float32))
+
+
 # ------------------------------------------------------------------ attention
 def _bits(a):
     return wl.f32_to_bf16_bits(np.asarray(a, np.float32))
@@ -381,6 +472,8 @@ def all_pins(lib, include_slow=False):
     check_special_cases(lib)
     check_metamorphic(lib)
     check_score_blocks(lib)
+    check_quantize_q8(lib)
+    check_select_q8(lib)
     check_attend(lib)
     if include_slow:
         check_exact_integer(wl.make("tiny"), lib)
