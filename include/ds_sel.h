@@ -165,6 +165,62 @@ int ds_sel_score_select_noalloc(int32_t device, uint32_t flags, const ds_sel_arg
  * `a` (-1 when a's sizes are invalid). */
 int64_t ds_sel_noalloc_scratch_bytes(const ds_sel_args* a);
 
+/* The 8-bit key stream (page "DeepSeek V4.1F Q4 on M3 Ultra with native
+ * DSpark MTP (40tps / 800tps)", paragraph "DSpark": the repository's kernels
+ * stream 8-bit weights in groups; this library reads that layout for the
+ * block keys).  Each key row of d values is cut into d/32 groups of 32; group
+ * g of block b holds 32 int8 codes c_i and one fp16 scale s, and stands for
+ * the values s * c_i.  The selection is the one ds_sel_score_select defines,
+ * with K[l][b][32 g + i] = s * c_i in place of the bf16 key; the block score
+ * is summed per group in fp32 and each group's sum multiplied by s (the
+ * folded query, weights and tie rule are unchanged).  Element strides. */
+typedef struct {
+  uint32_t struct_size;       /* sizeof(ds_sel_q8_keys) */
+  int32_t reserved;           /* 0 */
+  const int8_t* codes;        /* int8; block b of layer l at codes + l*code_layer_stride + b*ldc;
+                                 8-byte aligned; may be NULL only when N == 0 */
+  int64_t ldc;                /* >= d, multiple of 8 */
+  int64_t code_layer_stride;  /* multiple of 8; >= N*ldc when L > 1 */
+  const uint16_t* scales;     /* fp16 bits; block b of layer l at scales + l*scale_layer_stride
+                                 + b*lds, d/32 of them; may be NULL only when N == 0 */
+  int64_t lds;                /* >= d/32 */
+  int64_t scale_layer_stride; /* >= N*lds when L > 1 */
+} ds_sel_q8_keys;
+
+/* ds_sel_score_select over the 8-bit key stream `k8`; a->keys must be NULL
+ * (the keys come from k8), everything else of `a` and every rule of
+ * ds_sel_score_select (handle, stream, status codes) applies unchanged. */
+int ds_sel_score_select_q8(ds_sel* h, const ds_sel_args* a, const ds_sel_q8_keys* k8,
+                           void* hip_stream);
+
+/* The host-side checks ds_sel_score_select_q8 applies, without a device. */
+int ds_sel_check_args_q8(const ds_sel_limits* lim, const ds_sel_args* a, const ds_sel_q8_keys* k8);
+
+/* Quantise bf16 keys into the 8-bit key stream, per group of 32 values x_i
+ * with m = max |x_i|: s = the fp32 quotient m / 127 (correctly rounded),
+ * rounded to fp16 to nearest even; c_i = the fp32 quotient x_i / s rounded
+ * half away from zero and clamped to [-127, 127]; a group whose s is 0 (m = 0,
+ * or m / 127 below half the least fp16 subnormal) gets s = +0 and codes 0.
+ * The keys must be finite with |x| <= 127 * 65504 (larger ones give an
+ * infinite scale, which ds_sel_score_select_q8 does not accept).  Asynchronous
+ * on `hip_stream` on the current device; no handle.  DS_SEL_E_INVALID for bad
+ * sizes, strides or alignment. */
+typedef struct {
+  uint32_t struct_size;       /* sizeof(ds_sel_quantize_args) */
+  int32_t layers;             /* L >= 1 */
+  int32_t dim;                /* d in {32, 64, 128, 256} */
+  int32_t reserved;           /* 0 */
+  int64_t blocks;             /* N, 0 .. DS_SEL_MAX_BLOCKS */
+  const void* keys;           /* bf16, as in ds_sel_args (16-byte aligned, ldk multiple of 8) */
+  int64_t ldk, key_layer_stride;
+  int8_t* codes;              /* 16-byte aligned; ldc >= d and code_layer_stride both multiples of 16 */
+  int64_t ldc, code_layer_stride;
+  uint16_t* scales;           /* 2-byte aligned; lds >= d/32 */
+  int64_t lds, scale_layer_stride;
+} ds_sel_quantize_args;
+
+int ds_sel_quantize_q8(const ds_sel_quantize_args* a, void* hip_stream);
+
 /* Attention over a selection -- the step that consumes it (page "DeepSeek
  * V4.1F Q4 on M3 Ultra with native DSpark MTP (40tps / 800tps)", paragraph
  * "Decode at depth": each layer's compressed attention works on the blocks

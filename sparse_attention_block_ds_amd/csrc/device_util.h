@@ -34,6 +34,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// 8-bit keys: eight signed codes (two 32-bit words) as eight bf16 values,
+// exactly (|code| <= 128 has at most 8 significant bits): each code widens to
+// fp32 and keeps its top 16 bits.
+__device__ __forceinline__ uint32_t bf16_pair_of_codes(uint32_t w, int shift) {
+  const float a = (float)(int8_t)(w >> shift);
+  const float b = (float)(int8_t)(w >> (shift + 8));
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+}
+
+// fp16 bits widened to fp32 (exact).
+__device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
 // Bits of mask word j (blocks 32j .. 32j+31) that lie below `lim`.
 __device__ __forceinline__ uint32_t below_limit_bits(int64_t j, int64_t lim) {
   const int64_t lo = j * 32;

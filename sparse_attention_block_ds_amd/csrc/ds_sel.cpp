@@ -80,7 +80,9 @@ int check_limits(const ds_sel_limits* lim) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_args(const ds_sel_limits& lim, const ds_sel_args* a) {
+int check_q8_keys(const ds_sel_args* a, const ds_sel_q8_keys* k8);
+
+int check_args(const ds_sel_limits& lim, const ds_sel_args* a, const ds_sel_q8_keys* k8 = nullptr) {
   if (!a || a->struct_size != sizeof(ds_sel_args)) return DS_SEL_E_INVALID;
   if (a->layers < 1 || a->rows < 1 || a->heads < 1 || a->dim < 1 || a->k < 1 || a->blocks < 0)
     return DS_SEL_E_INVALID;
@@ -100,7 +102,11 @@ int check_args(const ds_sel_limits& lim, const ds_sel_args* a) {
       !aligned(a->mask, 4))
     return DS_SEL_E_INVALID;
   const int64_t N = a->blocks;
-  if (N > 0) {
+  if (k8) {
+    if (a->keys) return DS_SEL_E_INVALID;  // the key stream comes from k8
+    const int rc = check_q8_keys(a, k8);
+    if (rc != DS_SEL_OK) return rc;
+  } else if (N > 0) {
     if (!a->keys || !aligned(a->keys, 16)) return DS_SEL_E_INVALID;
     if (a->ldk < a->dim || a->ldk % 8 != 0) return DS_SEL_E_INVALID;
     if (a->key_layer_stride < 0 || a->key_layer_stride % 8 != 0) return DS_SEL_E_INVALID;
@@ -113,6 +119,21 @@ int check_args(const ds_sel_limits& lim, const ds_sel_args* a) {
     if (a->layers > 1 && a->mask_layer_stride < (a->rows - 1) * a->mask_row_stride + words)
       return DS_SEL_E_INVALID;
   }
+  return DS_SEL_OK;
+}
+
+// The 8-bit key stream of a call: codes [L][N][ldc] int8 (8-byte aligned rows),
+// fp16 scales [L][N][lds] with d/32 per row.
+int check_q8_keys(const ds_sel_args* a, const ds_sel_q8_keys* k8) {
+  if (!k8 || k8->struct_size != sizeof(ds_sel_q8_keys) || k8->reserved != 0) return DS_SEL_E_INVALID;
+  const int64_t N = a->blocks, groups = a->dim / 32;
+  if (N == 0) return DS_SEL_OK;
+  if (!k8->codes || !aligned(k8->codes, 8) || !k8->scales || !aligned(k8->scales, 2)) return DS_SEL_E_INVALID;
+  if (k8->ldc < a->dim || k8->ldc % 8 != 0 || k8->code_layer_stride < 0 || k8->code_layer_stride % 8 != 0)
+    return DS_SEL_E_INVALID;
+  if (k8->lds < groups || k8->scale_layer_stride < 0) return DS_SEL_E_INVALID;
+  if (a->layers > 1 && (k8->code_layer_stride < N * k8->ldc || k8->scale_layer_stride < N * k8->lds))
+    return DS_SEL_E_INVALID;
   return DS_SEL_OK;
 }
 
@@ -272,7 +293,8 @@ int mark_done(hipEvent_t done, hipStream_t stream) {
   if (st != hipStreamCaptureStatusNone) return DS_SEL_OK;
   return hipEventRecord(done, stream) == hipSuccess ? DS_SEL_OK : DS_SEL_E_HIP;
 }
-int enqueue(const Target& t, const ds_sel_args* a, void* hip_stream, void* const* events);
+int enqueue(const Target& t, const ds_sel_args* a, void* hip_stream, void* const* events,
+            const ds_sel_q8_keys* k8 = nullptr);
 
 Target handle_target(const ds_sel* h) {
   Target t;
@@ -341,6 +363,57 @@ int ds_sel_score_select_profiled(ds_sel* h, const ds_sel_args* a, void* hip_stre
   const int rc = check_args(h->lim, a);
   if (rc != DS_SEL_OK) return rc;
   return enqueue(handle_target(h), a, hip_stream, events);
+}
+
+int ds_sel_score_select_q8(ds_sel* h, const ds_sel_args* a, const ds_sel_q8_keys* k8, void* hip_stream) {
+  if (!h || !k8) return DS_SEL_E_INVALID;
+  const int rc = check_args(h->lim, a, k8);
+  if (rc != DS_SEL_OK) return rc;
+  return enqueue(handle_target(h), a, hip_stream, nullptr, k8);
+}
+
+int ds_sel_check_args_q8(const ds_sel_limits* lim, const ds_sel_args* a, const ds_sel_q8_keys* k8) {
+  const int rc = check_limits(lim);
+  if (rc != DS_SEL_OK) return rc;
+  if (!k8) return DS_SEL_E_INVALID;
+  return check_args(*lim, a, k8);
+}
+
+int ds_sel_quantize_q8(const ds_sel_quantize_args* a, void* hip_stream) {
+  if (!a || a->struct_size != sizeof(ds_sel_quantize_args) || a->reserved != 0) return DS_SEL_E_INVALID;
+  if (a->layers < 1 || a->blocks < 0 || a->blocks > DS_SEL_MAX_BLOCKS) return DS_SEL_E_INVALID;
+  if (a->dim != 32 && a->dim != 64 && a->dim != 128 && a->dim != 256) return DS_SEL_E_INVALID;
+  if (a->blocks > 0) {
+    if (!a->keys || !aligned(a->keys, 16) || !a->codes || !aligned(a->codes, 16) || !a->scales ||
+        !aligned(a->scales, 2))
+      return DS_SEL_E_INVALID;
+    if (a->ldk < a->dim || a->ldk % 8 != 0 || a->key_layer_stride < 0 || a->key_layer_stride % 8 != 0)
+      return DS_SEL_E_INVALID;
+    if (a->ldc < a->dim || a->ldc % 16 != 0 || a->code_layer_stride < 0 || a->code_layer_stride % 16 != 0)
+      return DS_SEL_E_INVALID;
+    if (a->lds < a->dim / 32 || a->scale_layer_stride < 0) return DS_SEL_E_INVALID;
+    if (a->layers > 1 && (a->key_layer_stride < a->blocks * a->ldk ||
+                          a->code_layer_stride < a->blocks * a->ldc ||
+                          a->scale_layer_stride < a->blocks * a->lds))
+      return DS_SEL_E_INVALID;
+  }
+  int current = 0;
+  if (hipGetDevice(&current) != hipSuccess) return DS_SEL_E_NODEVICE;
+  dssel::QuantizeCall c{};
+  c.layers = a->layers;
+  c.dim = a->dim;
+  c.blocks = a->blocks;
+  c.keys = static_cast<const uint16_t*>(a->keys);
+  c.ldk = a->ldk;
+  c.key_layer_stride = a->key_layer_stride;
+  c.codes = a->codes;
+  c.ldc = a->ldc;
+  c.code_layer_stride = a->code_layer_stride;
+  c.scales = a->scales;
+  c.lds = a->lds;
+  c.scale_layer_stride = a->scale_layer_stride;
+  return dssel::launch_quantize(c, static_cast<hipStream_t>(hip_stream)) == hipSuccess ? (int)DS_SEL_OK
+                                                                                      : (int)DS_SEL_E_HIP;
 }
 
 int64_t ds_sel_noalloc_scratch_bytes(const ds_sel_args* a) {
@@ -496,7 +569,8 @@ int ds_sel_attend(ds_sel* h, const ds_sel_attend_args* a, void* hip_stream) {
 
 namespace {
 // Enqueue the chain for an already validated call on the target's scratch.
-int enqueue(const Target& t, const ds_sel_args* a, void* hip_stream, void* const* events) {
+int enqueue(const Target& t, const ds_sel_args* a, void* hip_stream, void* const* events,
+            const ds_sel_q8_keys* k8) {
   dssel::Call c{};
   c.layers = a->layers;
   c.rows = a->rows;
@@ -517,6 +591,15 @@ int enqueue(const Target& t, const ds_sel_args* a, void* hip_stream, void* const
                     : ((a->mask_row_stride == 0 || a->rows == 1) ? dssel::kSharedMask
                                                                  : dssel::kRowMask);
   c.engine = (t.flags & DS_SEL_FLAG_VALU_SCORE) ? dssel::kEngineValu : dssel::kEngineMfma;
+  c.fmt = k8 ? dssel::kKeysQ8 : dssel::kKeysBf16;
+  if (k8) {
+    c.codes = k8->codes;
+    c.ldc = k8->ldc;
+    c.code_layer_stride = k8->code_layer_stride;
+    c.scales = k8->scales;
+    c.lds = k8->lds;
+    c.scale_layer_stride = k8->scale_layer_stride;
+  }
   c.ntiles = (int32_t)((a->blocks + dssel::kTileBlocks - 1) / dssel::kTileBlocks);
   c.cand_stride = (a->blocks + 3) / 4 * 4;
   {

@@ -45,6 +45,11 @@ enum AdmitMode : int {
   kRowMask = 2,     // a mask row per query row: one union list, per-row admission
 };
 
+enum KeyFormat : int {
+  kKeysBf16 = 0,  // bf16 key rows
+  kKeysQ8 = 1,    // groups of 32 int8 codes, one fp16 scale per group
+};
+
 enum Engine : int {
   kEngineMfma = 0,  // bf16 matrix cores on an exact 3-way bf16 split of the fp32 q~
   kEngineValu = 1,  // fp32 FMAs on the vector ALUs
@@ -69,6 +74,12 @@ struct Call {
   int32_t* out_idx;
   float* out_score;
   int32_t* out_count;
+  // 8-bit keys (fmt == kKeysQ8): codes [L][N][ldc], fp16 scales [L][N][lds]
+  int32_t fmt;
+  const int8_t* codes;
+  int64_t ldc, code_layer_stride;
+  const uint16_t* scales;
+  int64_t lds, scale_layer_stride;
   // scratch (owned by the handle), laid out with this call's dimensions
   float* qt;           // [L][R][d] folded query rows, fp32
   uint16_t* qparts;    // [L][3][R][d] bf16 hi/mid/lo parts of q~ (hi + mid + lo == q~)
@@ -109,6 +120,19 @@ struct AttendCall {
 };
 
 hipError_t launch_attend(const AttendCall& c, hipStream_t stream);
+
+// Quantising bf16 key rows into the 8-bit stream (ds_sel_quantize_q8).
+struct QuantizeCall {
+  int32_t layers, dim;
+  int64_t blocks;
+  const uint16_t* keys;
+  int64_t ldk, key_layer_stride;
+  int8_t* codes;
+  int64_t ldc, code_layer_stride;
+  uint16_t* scales;
+  int64_t lds, scale_layer_stride;
+};
+hipError_t launch_quantize(const QuantizeCall& c, hipStream_t stream);
 
 // Calibration launches (an empty kernel, a plain read of every key row, a
 // gather of the admitted key rows); see ds_sel_calibrate.

@@ -213,6 +213,94 @@ struct SampleMfma {
   }
 };
 
+// The same sampled scores on 8-bit keys: each 32-column group is one MFMA
+// with its own accumulation (codes widened exactly to bf16), scaled by the
+// block's group scale and summed in fp32.
+template <int R, int D>
+struct SampleMfmaQ8 {
+  static constexpr int KC = D / 32;
+  uint2 kb[kGroupsPerWave][KC];
+  uint16_t ks[kGroupsPerWave][KC];
+  uint32_t mw[kGroupsPerWave][4];
+
+  __device__ void issue(const Call& c, int l, int64_t n, const uint32_t* mask_l, int S) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int8_t* codes = c.codes + (int64_t)l * c.code_layer_stride;
+    const uint16_t* scales = c.scales + (int64_t)l * c.scale_layer_stride;
+#pragma unroll
+    for (int g = 0; g < kGroupsPerWave; ++g) {
+      const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) {
+        kb[g][cc] = make_uint2(0u, 0u);
+        ks[g][cc] = 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mw[g][i] = 0xFFFFFFFFu;
+      if (j < S) {
+        const int64_t b = sample_block(j, n);
+        const int8_t* row = codes + b * c.ldc + 8 * (lane >> 4);
+#pragma unroll
+        for (int cc = 0; cc < KC; ++cc) {
+          kb[g][cc] = *reinterpret_cast<const uint2*>(row + 32 * cc);
+          ks[g][cc] = scales[b * c.lds + cc];
+        }
+        if (c.mode == kSharedMask) {
+          const uint32_t w = mask_l[b >> 5];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mw[g][i] = w;
+        } else if (c.mode == kRowMask) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * (lane >> 4) + i;
+            if (r < R) mw[g][i] = mask_l[r * c.mask_row_stride + (b >> 5)];
+          }
+        }
+      }
+    }
+  }
+
+  __device__ void finish(int64_t n, int S, FoldShared& sh) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int m = lane & 15;
+    bf16x8_t a[KC];
+#pragma unroll
+    for (int cc = 0; cc < KC; ++cc) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (m < R) {
+        const float* qr = &sh.q[m < R ? m : 0][32 * cc + 8 * (lane >> 4)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = (uint32_t)f32_to_bf16_rne(qr[2 * e]) | ((uint32_t)f32_to_bf16_rne(qr[2 * e + 1]) << 16);
+      }
+      a[cc] = __builtin_bit_cast(bf16x8_t, v);
+    }
+#pragma unroll
+    for (int g = 0; g < kGroupsPerWave; ++g) {
+      const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
+      float sc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) {
+        const u32x4_t bv = {bf16_pair_of_codes(kb[g][cc].x, 0), bf16_pair_of_codes(kb[g][cc].x, 16),
+                            bf16_pair_of_codes(kb[g][cc].y, 0), bf16_pair_of_codes(kb[g][cc].y, 16)};
+        const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a[cc], __builtin_bit_cast(bf16x8_t, bv), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const float scale = half_bits_to_f32(ks[g][cc]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] += scale * acc[i];
+      }
+      if (j < S) {
+        const int64_t b = sample_block(j, n);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * (lane >> 4) + i;
+          if (r < R && b < sh.lim[r] && ((mw[g][i] >> (b & 31)) & 1u)) sh.skey[r][j] = score_to_key(sc[i]);
+        }
+      }
+    }
+  }
+};
+
 // A floor for the j-th largest of the 512 keys a wave holds (8 per lane): the
 // largest x with at least j keys >= x, built bit by bit from the top, over
 // the top 16 bits only (sign, exponent and 7 mantissa bits of the score).
@@ -234,7 +322,7 @@ __device__ __forceinline__ uint32_t wave_jth_largest(const uint32_t (&v)[kSample
 // Workgroup 0 of layer l: counts, fold, floors.  Every global load the
 // workgroup needs (sampled key rows and their mask words, the query heads and
 // weights, the mask words to count) is issued before any of them is used.
-template <int R, int D>
+template <int R, int D, class Sampler>
 __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
   const int H = c.heads;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -246,7 +334,7 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
   // nothing (samples at or past a row's limit are simply not admitted).
   const int64_t N = c.blocks;
   const int S = N < kSampleSlots ? (int)N : kSampleSlots;
-  SampleMfma<R, D> smp;
+  Sampler smp;
   smp.issue(c, l, N, mask_l, S);
 
   // The mask words to count, when every row shares one mask row (all words
@@ -436,23 +524,31 @@ __device__ void expand_tiles(const Call& c, int l, int x, ExpandShared& sh) {
   for (int i = lane; i < tile_total; i += kWave) out[i] = sh.stage[wave][i];
 }
 
-template <int R, int D>
+template <int R, int D, class Sampler>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(Call c) {
   __shared__ PrepShared sh;
   // blockIdx.x is the layer, so that consecutive workgroups (which the
   // dispatcher deals out to the XCDs in turn) belong to different layers and
   // the layers' fold workgroups spread over every XCD.
-  if (blockIdx.y == 0) fold_count_floor<R, D>(c, blockIdx.x, sh.f);
+  if (blockIdx.y == 0) fold_count_floor<R, D, Sampler>(c, blockIdx.x, sh.f);
   else expand_tiles<R>(c, blockIdx.x, blockIdx.y, sh.e);
+}
+
+template <int R, int D>
+void launch_rd(const Call& c, dim3 grid, hipStream_t stream) {
+  if (c.fmt == kKeysQ8)
+    hipLaunchKernelGGL((prep_kernel<R, D, SampleMfmaQ8<R, D>>), grid, dim3(kPrepThreads), 0, stream, c);
+  else
+    hipLaunchKernelGGL((prep_kernel<R, D, SampleMfma<R, D>>), grid, dim3(kPrepThreads), 0, stream, c);
 }
 
 template <int R>
 hipError_t launch_r(const Call& c, dim3 grid, hipStream_t stream) {
   switch (c.dim) {
-    case 32: hipLaunchKernelGGL((prep_kernel<R, 32>), grid, dim3(kPrepThreads), 0, stream, c); break;
-    case 64: hipLaunchKernelGGL((prep_kernel<R, 64>), grid, dim3(kPrepThreads), 0, stream, c); break;
-    case 128: hipLaunchKernelGGL((prep_kernel<R, 128>), grid, dim3(kPrepThreads), 0, stream, c); break;
-    case 256: hipLaunchKernelGGL((prep_kernel<R, 256>), grid, dim3(kPrepThreads), 0, stream, c); break;
+    case 32: launch_rd<R, 32>(c, grid, stream); break;
+    case 64: launch_rd<R, 64>(c, grid, stream); break;
+    case 128: launch_rd<R, 128>(c, grid, stream); break;
+    case 256: launch_rd<R, 256>(c, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -125,7 +125,7 @@ struct PieceCtx {
   }
 
   // Lane r (< R) gets the number of staged entries of row r.
-  __device__ int count_rows() const {
+  __device__ __forceinline__ int count_rows() const {
     const int lane = lane_id();
     int mine = 0;
     for (int i0 = 0; i0 < nst; i0 += kWave) {
@@ -142,7 +142,7 @@ struct PieceCtx {
 
   // Copy the staged entries out; lane r (< R) holds the first slot of row r's
   // run in the row's list.  Entries keep their staging order within a row.
-  __device__ void write_out(int start) const {
+  __device__ __forceinline__ void write_out(int start) const {
     const int lane = lane_id();
     int run = start;  // lane r: next free slot of row r
     for (int i0 = 0; i0 < nst; i0 += kWave) {
@@ -250,6 +250,112 @@ struct MfmaEngine {
 
   // The lane's rows of the MFMA output (row 4 s + lane / 16 of set s): their
   // admitted counts (0 past R) and floors.
+  int lp[S];
+  uint32_t lf[S];
+  __device__ void bind_rows(const ScoreShared<R>& sh) {
+    const int g = lane_id() >> 4;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int r = 4 * s + g;
+      lp[s] = r < R ? sh.P[r] : 0;
+      lf[s] = r < R ? sh.floor[r] : 0u;
+    }
+  }
+};
+
+// ------------------------------------------------------- MFMA engine, 8-bit keys
+// The same A operand (q~ as three exact bf16 parts along M) against 8-bit key
+// rows: group g of a row is 32 int8 codes c with one fp16 scale s, standing
+// for the values s c.  Each 32-column chunk is one group, so each chunk gets
+// its own accumulation: the codes widen exactly to bf16 (B operand), one
+// v_mfma_f32_16x16x32_bf16 per row set gives sum_i q~_i c_i over the group
+// (exact products), and the lane adds s times that sum to its row's score.
+// Each lane loads 8 codes (8 bytes) per chunk of its block and the block's
+// group scales.
+template <int R, int D, int NBUF>
+struct MfmaQ8Engine {
+  static constexpr int kRows = R, kBuffers = NBUF;
+  static constexpr int KC = D / 32;       // 32-column groups of a key row
+  static constexpr int S = (R + 3) / 4;   // MFMA row sets
+  bf16x8_t a[S][KC];
+  uint2 buf[NBUF][KC];                    // codes: 8 of the lane's block per group
+  uint32_t sbuf[NBUF][(KC + 1) / 2];      // the block's group scales, two fp16 per word
+  const int8_t* codes_l;
+  const uint16_t* scales_l;
+  int64_t ldc, lds;
+
+  __device__ void init(const Call& c, int l) {
+    const int lane = lane_id();
+    const int m = lane & 15, g = lane >> 4;
+    const int p = m & 3;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int r = 4 * s + (m >> 2);
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (p < 3 && r < R)
+          v = load16(c.qparts + (((int64_t)l * 3 + p) * R + r) * D + 32 * cc + 8 * g);
+        a[s][cc] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+    codes_l = c.codes + (int64_t)l * c.code_layer_stride;
+    scales_l = c.scales + (int64_t)l * c.scale_layer_stride;
+    ldc = c.ldc;
+    lds = c.lds;
+  }
+
+  template <int B>
+  __device__ __forceinline__ void load(const PieceCtx<R>& t, const uint16_t*, int64_t, int g0) {
+    const int lane = lane_id();
+    const int e = g0 + (lane & 15);
+    if (t.valid(e)) {
+      const int64_t b = t.block_of(e);
+      const int8_t* row = codes_l + b * ldc + 8 * (lane >> 4);
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) buf[B][cc] = *reinterpret_cast<const uint2*>(row + 32 * cc);
+      const uint16_t* sr = scales_l + b * lds;
+#pragma unroll
+      for (int h = 0; h < (KC + 1) / 2; ++h)
+        sbuf[B][h] = (uint32_t)sr[2 * h] | (2 * h + 1 < KC ? (uint32_t)sr[2 * h + 1] << 16 : 0u);
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) buf[B][cc] = make_uint2(0u, 0u);
+#pragma unroll
+      for (int h = 0; h < (KC + 1) / 2; ++h) sbuf[B][h] = 0u;
+    }
+  }
+
+  template <int B>
+  __device__ __forceinline__ void compute_emit(PieceCtx<R>& t, int g0) {
+    float score[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) score[s] = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < KC; ++cc) {
+      const u32x4_t bv = {bf16_pair_of_codes(buf[B][cc].x, 0), bf16_pair_of_codes(buf[B][cc].x, 16),
+                          bf16_pair_of_codes(buf[B][cc].y, 0), bf16_pair_of_codes(buf[B][cc].y, 16)};
+      const float scale = half_bits_to_f32((uint16_t)(sbuf[B][cc / 2] >> (16 * (cc & 1))));
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a[s][cc], __builtin_bit_cast(bf16x8_t, bv), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        score[s] += scale * ((acc[0] + acc[1]) + acc[2]);
+      }
+    }
+    const int lane = lane_id();
+    const int e = g0 + (lane & 15), g = lane >> 4;
+    const int pos = t.pos_of(e);
+    const bool live = e < t.cnt;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint32_t key = score_to_key(score[s]);
+      bool ok = live && pos < lp[s] && key >= lf[s];
+      if (t.mode == kRowMask && ok) ok = t.row_admits(4 * s + g, e);
+      t.append(ok, key, pos, 4 * s + g);
+    }
+  }
+
   int lp[S];
   uint32_t lf[S];
   __device__ void bind_rows(const ScoreShared<R>& sh) {
@@ -379,7 +485,7 @@ struct Piece {
   int layer, j, pn, T;  // piece j of the pn pieces of `layer` (layer < 0: nothing to do)
 };
 
-__device__ Piece find_piece(const Call& c, int* shared_out) {
+__device__ __forceinline__ Piece find_piece(const Call& c, int* shared_out) {
   const int lane = lane_id();
   if (threadIdx.x < kWave) {
     const int L = c.layers;
@@ -485,8 +591,8 @@ __device__ __forceinline__ void score_body(const Call& c) {
   pc.stride = c.cand_stride;
   pc.mask_l = c.mask ? c.mask + (int64_t)sl * c.mask_layer_stride : nullptr;
   pc.mask_row_stride = c.mask_row_stride;
-  stream_piece<Engine::kBuffers>(eng, pc, c.keys + (int64_t)sl * c.key_layer_stride, c.ldk,
-                                 wave * kGroup, kWaves * kGroup);
+  stream_piece<Engine::kBuffers>(eng, pc, c.keys ? c.keys + (int64_t)sl * c.key_layer_stride : nullptr,
+                                 c.ldk, wave * kGroup, kWaves * kGroup);
   // End of the piece: one counter update per row for the whole workgroup.
   const int lane = lane_id();
   const int mine = pc.count_rows();  // lane r: this wave's staged entries of row r
@@ -507,12 +613,13 @@ __device__ __forceinline__ void score_body(const Call& c) {
   pc.write_out(start);
 }
 
-// The MFMA kernel is held to 128 registers (four waves per SIMD, 16 per
-// compute unit: the memory parallelism the stream needs); it fits without
-// spilling at d <= 128.  The vector-ALU kernel would spill there and is left
-// unconstrained.
-template <int R, int D, class Engine>
-__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+// The MFMA kernel is held to at least W waves per SIMD: 4 (128 registers, 16
+// waves per compute unit: the memory parallelism the stream needs) at
+// d <= 128; at d = 256 the A operand and the ring need more, so 3 (168
+// registers) up to four rows and 2 above, where the A operand alone takes 64.
+// No instantiation spills.  The vector-ALU kernel is left unconstrained.
+template <int R, int D, class Engine, int W>
+__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(W, 8)))
 void score_kernel_mfma(Call c) {
   score_body<R, D, Engine>(c);
 }
@@ -522,15 +629,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_valu(Call c) {
   score_body<R, D, Engine>(c);
 }
 
-constexpr int kRing = 3;  // load buffers per wave: two groups of key rows in flight
+// Load buffers per wave: two groups of key rows in flight; one at d = 256,
+// where a third buffer of 16-byte bf16 chunks (32 registers) does not fit.
+template <int D>
+constexpr int kRing = D >= 256 ? 2 : 3;
 
 template <int R, int D>
 hipError_t launch_rd(const Call& c, dim3 grid, hipStream_t s) {
-  if (c.engine == kEngineValu)
-    hipLaunchKernelGGL((score_kernel_valu<R, D, ValuEngine<R, D, kRing>>), grid,
+  constexpr int kMfmaWaves = D < 256 ? 4 : (R > 4 ? 2 : 3);
+  if (c.fmt == kKeysQ8)
+    hipLaunchKernelGGL((score_kernel_mfma<R, D, MfmaQ8Engine<R, D, kRing<D>>, kMfmaWaves>), grid,
+                       dim3(kScoreThreads), 0, s, c);
+  else if (c.engine == kEngineValu)
+    hipLaunchKernelGGL((score_kernel_valu<R, D, ValuEngine<R, D, kRing<D>>>), grid,
                        dim3(kScoreThreads), 0, s, c);
   else
-    hipLaunchKernelGGL((score_kernel_mfma<R, D, MfmaEngine<R, D, kRing>>), grid,
+    hipLaunchKernelGGL((score_kernel_mfma<R, D, MfmaEngine<R, D, kRing<D>>, kMfmaWaves>), grid,
                        dim3(kScoreThreads), 0, s, c);
   return hipGetLastError();
 }

@@ -247,7 +247,7 @@ static __device__ int rescore_row(const Call& c, int l, int r, uint64_t* words, 
   const int P = c.mode == kRowMask ? c.counts[(int64_t)l * kCountStride + kMaxRows]
                                    : c.counts[(int64_t)l * kCountStride + r];
   const int32_t* list = c.list + (int64_t)l * N;
-  const uint16_t* K = c.keys + (int64_t)l * c.key_layer_stride;
+  const uint16_t* K = c.keys ? c.keys + (int64_t)l * c.key_layer_stride : nullptr;
   int64_t lim = c.limit ? (int64_t)c.limit[lr] : N;
   lim = lim < 0 ? 0 : (lim > N ? N : lim);
   const uint32_t* mrow =
@@ -265,7 +265,18 @@ static __device__ int rescore_row(const Call& c, int l, int r, uint64_t* words, 
       if (mrow) adm = ((mrow[b >> 5] >> (b & 31)) & 1u) && (int64_t)b < lim;
     }
     uint64_t w = 0;
-    if (adm) {
+    if (adm && c.fmt == kKeysQ8) {
+      // 8-bit keys: per 32-column group, sum q~_i c_i, then add scale times that
+      const int8_t* crow = c.codes + (int64_t)l * c.code_layer_stride + (int64_t)b * c.ldc;
+      const uint16_t* srow = c.scales + (int64_t)l * c.scale_layer_stride + (int64_t)b * c.lds;
+      float dot = 0.0f;
+      for (int g = 0; g < D / 32; ++g) {
+        float t = 0.0f;
+        for (int i = 0; i < 32; ++i) t = fmaf(sh.q[32 * g + i], (float)crow[32 * g + i], t);
+        dot += half_bits_to_f32(srow[g]) * t;
+      }
+      w = pack(score_to_key(dot), p);
+    } else if (adm) {
       const uint16_t* krow = K + (int64_t)b * c.ldk;
       float dot = 0.0f;
       for (int i = 0; i < D; i += 8) {

@@ -27,7 +27,8 @@ DS_SEL_FLAG_VALU_SCORE = 1
 EXPORTED = ("ds_sel_create", "ds_sel_score_select", "ds_sel_score_select_profiled",
             "ds_sel_destroy", "ds_sel_check_args", "ds_sel_scratch_bytes", "ds_sel_status_string",
             "ds_sel_attend", "ds_sel_check_attend_args", "ds_sel_calibrate",
-            "ds_sel_score_select_noalloc", "ds_sel_noalloc_scratch_bytes")
+            "ds_sel_score_select_noalloc", "ds_sel_noalloc_scratch_bytes",
+            "ds_sel_score_select_q8", "ds_sel_check_args_q8", "ds_sel_quantize_q8")
 
 DS_SEL_CALIB_EMPTY = 0
 DS_SEL_CALIB_READ = 1
@@ -75,6 +76,23 @@ class CalibArgs(ctypes.Structure):
                 ("sink", ctypes.c_void_p)]
 
 
+class Q8Keys(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("reserved", ctypes.c_int32),
+                ("codes", ctypes.c_void_p), ("ldc", ctypes.c_int64),
+                ("code_layer_stride", ctypes.c_int64), ("scales", ctypes.c_void_p),
+                ("lds", ctypes.c_int64), ("scale_layer_stride", ctypes.c_int64)]
+
+
+class QuantizeArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("layers", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("reserved", ctypes.c_int32), ("blocks", ctypes.c_int64),
+                ("keys", ctypes.c_void_p), ("ldk", ctypes.c_int64),
+                ("key_layer_stride", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("ldc", ctypes.c_int64), ("code_layer_stride", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("lds", ctypes.c_int64),
+                ("scale_layer_stride", ctypes.c_int64)]
+
+
 class DsSelError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -120,6 +138,12 @@ def load_library(path: Optional[str] = None):
     lib.ds_sel_noalloc_scratch_bytes.restype = ctypes.c_int64
     lib.ds_sel_calibrate.argtypes = [P(CalibArgs), ctypes.c_void_p]
     lib.ds_sel_calibrate.restype = ctypes.c_int
+    lib.ds_sel_score_select_q8.argtypes = [ctypes.c_void_p, P(Args), P(Q8Keys), ctypes.c_void_p]
+    lib.ds_sel_score_select_q8.restype = ctypes.c_int
+    lib.ds_sel_check_args_q8.argtypes = [P(Limits), P(Args), P(Q8Keys)]
+    lib.ds_sel_check_args_q8.restype = ctypes.c_int
+    lib.ds_sel_quantize_q8.argtypes = [P(QuantizeArgs), ctypes.c_void_p]
+    lib.ds_sel_quantize_q8.restype = ctypes.c_int
     lib.ds_sel_status_string.argtypes = [ctypes.c_int]
     lib.ds_sel_status_string.restype = ctypes.c_char_p
     if default:
@@ -158,20 +182,59 @@ def check_select_tensors(q, w, keys, k, mask=None, limit=None, out=None, device=
     strides or device differ from what ds_sel_score_select reads and writes.
     Raises ValueError; returns nothing."""
     import torch
-    _require(isinstance(k, int) and k >= 1, "k must be an int >= 1")
-    _require(q.dim() == 4 and q.dtype == torch.bfloat16 and q.is_contiguous(),
-             "q must be a contiguous bf16 tensor [L, R, H, d]")
-    device = q.device if device is None else torch.device(device)
+    _check_query(q, w)
     L, R, H, d = q.shape
-    _require(w.dtype == torch.bfloat16 and tuple(w.shape) == (L, R, H) and w.is_contiguous(),
-             "w must be a contiguous bf16 tensor [L, R, H]")
     _require(keys.dtype == torch.bfloat16 and keys.dim() == 3 and keys.shape[0] == L and
              keys.shape[2] >= d, "keys must be a bf16 tensor [L, N, ldk] with ldk >= d")
     N = keys.shape[1]
     if N > 0:  # an empty key tensor is never read, whatever its strides
         _require(keys.stride(2) == 1, "keys must have unit stride in the last dim")
         _require(N == 1 or keys.stride(1) >= d, "keys rows overlap (stride(1) < d)")
-    tensors = [(q, "q"), (w, "w"), (keys, "keys")]
+    _check_rest(q, w, N, k, mask, limit, out, device, [(keys, "keys")])
+
+
+def check_q8_tensors(codes, scales, L, d):
+    """The 8-bit key stream: codes int8 [L, N, ldc] and scales float16 (the
+    fp16 scale bits) [L, N, lds], unit stride in the last dim, ldc >= d and
+    lds >= d/32.  Raises ValueError; returns N."""
+    import torch
+    _require(d % 32 == 0, "the 8-bit key stream needs d to be a multiple of 32")
+    _require(codes.dtype == torch.int8 and codes.dim() == 3 and codes.shape[0] == L and
+             codes.shape[2] >= d, "codes must be an int8 tensor [L, N, ldc] with ldc >= d")
+    N = codes.shape[1]
+    _require(scales.dtype == torch.float16 and scales.dim() == 3 and scales.shape[0] == L and
+             scales.shape[1] == N and scales.shape[2] >= d // 32,
+             "scales must be a float16 tensor [L, N, lds] with lds >= d/32")
+    if N > 0:
+        _require(codes.stride(2) == 1 and scales.stride(2) == 1,
+                 "codes and scales must have unit stride in the last dim")
+        _require(N == 1 or (codes.stride(1) >= d and scales.stride(1) >= d // 32),
+                 "codes or scales rows overlap")
+    return N
+
+
+def check_select_q8_tensors(q, w, codes, scales, k, mask=None, limit=None, out=None, device=None):
+    """check_select_tensors for ds_sel_score_select_q8.  Raises ValueError."""
+    _check_query(q, w)
+    N = check_q8_tensors(codes, scales, q.shape[0], q.shape[3])
+    _check_rest(q, w, N, k, mask, limit, out, device, [(codes, "codes"), (scales, "scales")])
+
+
+def _check_query(q, w):
+    import torch
+    _require(q.dim() == 4 and q.dtype == torch.bfloat16 and q.is_contiguous(),
+             "q must be a contiguous bf16 tensor [L, R, H, d]")
+    L, R, H, d = q.shape
+    _require(w.dtype == torch.bfloat16 and tuple(w.shape) == (L, R, H) and w.is_contiguous(),
+             "w must be a contiguous bf16 tensor [L, R, H]")
+
+
+def _check_rest(q, w, N, k, mask, limit, out, device, keys_tensors):
+    import torch
+    _require(isinstance(k, int) and k >= 1, "k must be an int >= 1")
+    device = q.device if device is None else torch.device(device)
+    L, R, H, d = q.shape
+    tensors = [(q, "q"), (w, "w")] + list(keys_tensors)
     if mask is not None:
         _require(mask.dtype == torch.int32 and mask.dim() == 3 and mask.shape[0] == L and
                  mask.shape[1] in (1, R) and mask.shape[2] * 32 >= N and mask.stride(2) == 1,
@@ -230,17 +293,20 @@ def check_attend_tensors(qa, keys, values, idx, count, scale, out=None, device=N
         _on(t, device, name)
 
 
-def make_args(q, w, keys, k, mask=None, limit=None, out_idx=None, out_score=None, out_count=None):
-    """Fill an Args struct from tensors already accepted by check_select_tensors."""
+def make_args(q, w, keys, k, mask=None, limit=None, out_idx=None, out_score=None, out_count=None,
+              blocks=None):
+    """Fill an Args struct from tensors already accepted by check_select_tensors
+    (keys None, with `blocks` given, for the 8-bit key stream)."""
     L, R, H, d = q.shape
-    N = keys.shape[1]
+    N = keys.shape[1] if keys is not None else blocks
     a = Args()
     a.struct_size = ctypes.sizeof(Args)
     a.layers, a.rows, a.heads, a.dim, a.k, a.blocks = L, R, H, d, k, N
     a.q, a.w = _ptr(q), _ptr(w)
-    a.keys = _ptr(keys) if N > 0 else None
-    a.ldk = keys.stride(1)
-    a.key_layer_stride = keys.stride(0)
+    if keys is not None:
+        a.keys = _ptr(keys) if N > 0 else None
+        a.ldk = keys.stride(1)
+        a.key_layer_stride = keys.stride(0)
     if mask is not None:
         a.mask = _ptr(mask)
         a.mask_row_stride = 0 if mask.shape[1] == 1 else mask.stride(1)
@@ -248,6 +314,18 @@ def make_args(q, w, keys, k, mask=None, limit=None, out_idx=None, out_score=None
     a.limit = _ptr(limit)
     a.out_idx, a.out_score, a.out_count = _ptr(out_idx), _ptr(out_score), _ptr(out_count)
     return a
+
+
+def make_q8_keys(codes, scales):
+    """Fill a Q8Keys struct from tensors already accepted by check_q8_tensors."""
+    k8 = Q8Keys()
+    k8.struct_size = ctypes.sizeof(Q8Keys)
+    k8.reserved = 0
+    if codes.shape[1] > 0:
+        k8.codes, k8.scales = _ptr(codes), _ptr(scales)
+    k8.ldc, k8.code_layer_stride = codes.stride(1), codes.stride(0)
+    k8.lds, k8.scale_layer_stride = scales.stride(1), scales.stride(0)
+    return k8
 
 
 def make_attend_args(qa, keys, values, idx, count, scale, out):
@@ -332,6 +410,30 @@ class Selector:
             raise DsSelError(rc, "ds_sel_score_select")
         return out
 
+
+    def score_select_q8(self, q, w, codes, scales, k, mask=None, limit=None, out=None,
+                        stream=None):
+        """score_select over the 8-bit key stream (ds_sel_score_select_q8):
+        codes int8 [L,N,ldc] and scales float16 [L,N,lds] as quantize_q8
+        returns them; every other argument and the result as score_select."""
+        torch = self._torch
+        dev = torch.device("cuda", self.device)
+        check_select_q8_tensors(q, w, codes, scales, k, mask, limit, out, dev)
+        L, R = q.shape[0], q.shape[1]
+        if out is None:
+            out = (torch.empty((L, R, k), dtype=torch.int32, device=q.device),
+                   torch.empty((L, R, k), dtype=torch.float32, device=q.device),
+                   torch.empty((L, R), dtype=torch.int32, device=q.device))
+        a = make_args(q, w, None, k, mask, limit, *out, blocks=codes.shape[1])
+        k8 = make_q8_keys(codes, scales)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        rc = self.lib.ds_sel_score_select_q8(self.handle, ctypes.byref(a), ctypes.byref(k8),
+                                             ctypes.c_void_p(handle))
+        if rc != DS_SEL_OK:
+            raise DsSelError(rc, "ds_sel_score_select_q8")
+        return out
 
     def attend(self, qa, keys, values, idx, count, scale, out=None, stream=None):
         """Enqueue attention over a selection; returns out f32 [L,R,Ha,d].
@@ -419,3 +521,38 @@ def score_select_noalloc(q, w, keys, k, mask, limit, out, device=None, engine="m
     if rc != DS_SEL_OK:
         raise DsSelError(rc, "ds_sel_score_select_noalloc")
     return out
+
+
+def quantize_q8(keys, codes=None, scales=None, stream=None):
+    """ds_sel_quantize_q8: bf16 keys [L,N,ldk] (unit stride in the last dim)
+    into the 8-bit key stream; returns (codes int8 [L,N,d], scales float16
+    [L,N,d/32]), allocated here unless given (codes rows 16-byte aligned).
+    Asynchronous on `stream` (default: torch's current stream)."""
+    import torch
+    _require(keys.dtype == torch.bfloat16 and keys.dim() == 3, "keys must be a bf16 tensor [L, N, d]")
+    L, N, d = keys.shape
+    _require(N == 0 or keys.stride(2) == 1, "keys must have unit stride in the last dim")
+    if codes is None:
+        codes = torch.empty((L, N, d), dtype=torch.int8, device=keys.device)
+    if scales is None:
+        scales = torch.empty((L, N, d // 32), dtype=torch.float16, device=keys.device)
+    check_q8_tensors(codes, scales, L, d)
+    _require(codes.shape[1] == N, "codes must hold one row per key block")
+    for t, name in ((codes, "codes"), (scales, "scales")):
+        _on(t, keys.device, name)
+    lib = load_library()
+    a = QuantizeArgs()
+    a.struct_size = ctypes.sizeof(QuantizeArgs)
+    a.layers, a.dim, a.reserved, a.blocks = L, d, 0, N
+    if N > 0:
+        a.keys, a.codes, a.scales = _ptr(keys), _ptr(codes), _ptr(scales)
+    a.ldk, a.key_layer_stride = keys.stride(1), keys.stride(0)
+    a.ldc, a.code_layer_stride = codes.stride(1), codes.stride(0)
+    a.lds, a.scale_layer_stride = scales.stride(1), scales.stride(0)
+    if stream is None:
+        stream = torch.cuda.current_stream(keys.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    rc = lib.ds_sel_quantize_q8(ctypes.byref(a), ctypes.c_void_p(handle))
+    if rc != DS_SEL_OK:
+        raise DsSelError(rc, "ds_sel_quantize_q8")
+    return codes, scales

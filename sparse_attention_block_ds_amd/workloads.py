@@ -266,6 +266,23 @@ def make_custom(layers, rows, heads, dim, blocks, k, *, seed, values="normal", l
 # attention queries qa ~ N(0,1) and the values V ~ N(0,1), drawn in that order
 # from default_rng(seed + 100) and rounded to bf16 (nearest, ties to even).
 
+def random_q8_stream(layers, blocks, dim, *, seed, scale_exponents=None, scale_range=(1e-3, 0.05)):
+    """A random 8-bit key stream: codes int8 [L][N][d] uniform in [-127, 127]
+    and scales as fp16 bits [L][N][d/32], either 2**e with e drawn uniformly
+    from the integer range `scale_exponents` (lo, hi inclusive; dequantised
+    keys then exact in bf16 and every product exact) or uniform over
+    `scale_range` rounded to fp16."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(-127, 128, (layers, blocks, dim)).astype(np.int8)
+    shape = (layers, blocks, dim // 32)
+    if scale_exponents is not None:
+        lo, hi = scale_exponents
+        sc = (np.float32(2.0) ** rng.integers(lo, hi + 1, shape)).astype(np.float16)
+    else:
+        sc = rng.uniform(scale_range[0], scale_range[1], shape).astype(np.float16)
+    return codes, sc.view(np.uint16)
+
+
 def attend_inputs(layers, rows, heads, dim, blocks, *, seed, ldv=None):
     """(qa [L][R][Ha][d], values [L][N][ldv]) as bf16 bits; columns past d hold NaN bits."""
     rng = np.random.default_rng(seed + 100)

@@ -62,8 +62,31 @@ def assert_self_consistent(p: wl.Problem, gpu, k=None, rows=None):
         assert np.all(np.isfinite(sel_sc))
 
 
-def assert_general(p: wl.Problem, gpu, ora, pairs=None):
-    """The general-input acceptance rule against the oracle."""
+def upload_q8(codes, scales, device="cuda"):
+    """Device tensors of an 8-bit key stream: codes int8, scales float16 (fp16 bits kept)."""
+    import torch
+    c = torch.from_numpy(np.ascontiguousarray(codes)).to(device)
+    s = torch.from_numpy(np.ascontiguousarray(scales).view(np.float16)).to(device)
+    return c, s
+
+
+def run_gpu_q8(selector: sel.Selector, p: wl.Problem, codes, scales, k=None):
+    import torch
+    q, w, _, mask, limit = sel.upload(p)
+    c, s = upload_q8(codes, scales)
+    idx, score, count = selector.score_select_q8(q, w, c, s, p.k if k is None else k, mask, limit)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), score.cpu().numpy(), count.cpu().numpy()
+
+
+def run_oracle_q8(p: wl.Problem, codes, scales, k=None):
+    return oracle.select_q8(p.q, p.w, codes, scales, p.k if k is None else k, p.mask, p.limit)
+
+
+def assert_general(p: wl.Problem, gpu, ora, pairs=None, scorer=None):
+    """The general-input acceptance rule against the oracle.  `scorer(l, r,
+    blocks)` gives the oracle's per-block scores (default: the bf16 key
+    stream's oracle.score_blocks)."""
     idx, score, count = gpu
     o_idx, o_score, o_count = ora
     pairs = pairs if pairs is not None else [(l, r) for l in range(p.layers) for r in range(p.rows)]
@@ -73,7 +96,10 @@ def assert_general(p: wl.Problem, gpu, ora, pairs=None):
         if m == 0:
             continue
         g_blocks = idx[l, r, :m]
-        s_or = oracle.score_blocks(p.q, p.w, p.keys, l, r, g_blocks).astype(np.float64)
+        if scorer is None:
+            s_or = oracle.score_blocks(p.q, p.w, p.keys, l, r, g_blocks).astype(np.float64)
+        else:
+            s_or = np.asarray(scorer(l, r, g_blocks), np.float64)
         s_gpu = score[l, r, :m].astype(np.float64)
         err = np.abs(s_gpu - s_or)
         tol = ATOL + RTOL * np.abs(s_or)

@@ -322,13 +322,9 @@ def _q8_problem(seed, L, R, H, d, N, k, pow2_scales, values="normal", **kw):
     [-127, 127] and scales either powers of two (dequantised keys exact in bf16)
     or general fp16 values."""
     p = wl.make_custom(L, R, H, d, N, k, seed=seed, values=values, **kw)
-    rng = np.random.default_rng(seed + 1)
-    codes = rng.integers(-127, 128, (L, N, d)).astype(np.int8)
-    if pow2_scales:
-        sc = (np.float32(2.0) ** rng.integers(-10, 3, (L, N, d // 32))).astype(np.float16)
-    else:
-        sc = rng.uniform(1e-3, 0.05, (L, N, d // 32)).astype(np.float16)
-    return p, codes, sc.view(np.uint16)
+    codes, scales = wl.random_q8_stream(L, N, d, seed=seed + 1,
+                                        scale_exponents=(-10, 2) if pow2_scales else None)
+    return p, codes, scales
 
 
 def check_select_q8(lib):

@@ -52,6 +52,13 @@ def test_struct_layout_matches_header(tmp_path):
 int main(void) {
   printf("ds_sel_limits %zu\nds_sel_args %zu\n", sizeof(ds_sel_limits), sizeof(ds_sel_args));
   printf("ds_sel_attend_args %zu\n", sizeof(ds_sel_attend_args));
+  printf("ds_sel_q8_keys %zu\nds_sel_quantize_args %zu\n", sizeof(ds_sel_q8_keys),
+         sizeof(ds_sel_quantize_args));
+  F(ds_sel_q8_keys, codes); F(ds_sel_q8_keys, ldc); F(ds_sel_q8_keys, scales);
+  F(ds_sel_q8_keys, scale_layer_stride);
+  F(ds_sel_quantize_args, blocks); F(ds_sel_quantize_args, keys); F(ds_sel_quantize_args, codes);
+  F(ds_sel_quantize_args, code_layer_stride); F(ds_sel_quantize_args, scales);
+  F(ds_sel_quantize_args, scale_layer_stride);
   F(ds_sel_limits, max_blocks); F(ds_sel_args, blocks); F(ds_sel_args, q); F(ds_sel_args, ldk);
   F(ds_sel_args, mask); F(ds_sel_args, mask_layer_stride); F(ds_sel_args, limit);
   F(ds_sel_args, out_count);
@@ -69,8 +76,11 @@ int main(void) {
     assert int(lines["ds_sel_limits"]) == ctypes.sizeof(sel.Limits)
     assert int(lines["ds_sel_args"]) == ctypes.sizeof(sel.Args)
     assert int(lines["ds_sel_attend_args"]) == ctypes.sizeof(sel.AttendArgs)
+    assert int(lines["ds_sel_q8_keys"]) == ctypes.sizeof(sel.Q8Keys)
+    assert int(lines["ds_sel_quantize_args"]) == ctypes.sizeof(sel.QuantizeArgs)
     classes = {"ds_sel_limits": sel.Limits, "ds_sel_args": sel.Args,
-               "ds_sel_attend_args": sel.AttendArgs}
+               "ds_sel_attend_args": sel.AttendArgs, "ds_sel_q8_keys": sel.Q8Keys,
+               "ds_sel_quantize_args": sel.QuantizeArgs}
     for key, value in lines.items():
         if "." in key:
             struct, field = key.split(".")
@@ -294,3 +304,86 @@ def test_noalloc_checks_before_touching_a_device(lib):
     assert lib.ds_sel_score_select_noalloc(0, 4, ctypes.byref(small), None) == sel.DS_SEL_E_INVALID
     assert lib.ds_sel_score_select_noalloc(-1, 0, ctypes.byref(small), None) == sel.DS_SEL_E_INVALID
     assert lib.ds_sel_score_select_noalloc(0, 0, ctypes.byref(small), None) == sel.DS_SEL_E_NODEVICE
+
+
+# ------------------------------------------------------------ the 8-bit key stream
+def _q8(L=2, N=75000, d=128, ldc=None, lds=None):
+    ldc, lds = ldc or d, lds or d // 32
+    codes = FakeTensor((L, N, ldc), (N * ldc, ldc, 1), ptr=0xB0000)
+    scales = FakeTensor((L, N, lds), (N * lds, lds, 1), ptr=0xC0002)
+    return sel.make_q8_keys(codes, scales)
+
+
+def _q8_args(L=2, N=75000, d=128):
+    a = _args(L=L, N=N, d=d)
+    a.keys, a.ldk, a.key_layer_stride = None, 0, 0
+    return a
+
+
+def check_q8(lib, args, k8, **lim):
+    limits = sel.make_limits(**{**LIM, **lim})
+    return lib.ds_sel_check_args_q8(ctypes.byref(limits), ctypes.byref(args),
+                                    ctypes.byref(k8) if k8 is not None else None)
+
+
+def test_q8_valid_arguments_pass(lib):
+    assert check_q8(lib, _q8_args(), _q8()) == sel.DS_SEL_OK
+    assert check_q8(lib, _q8_args(d=64), _q8(d=64, ldc=72, lds=3)) == sel.DS_SEL_OK
+    assert check_q8(lib, _q8_args(L=1, d=32), _q8(L=1, d=32)) == sel.DS_SEL_OK
+    empty = _q8(N=0)
+    empty.codes = empty.scales = None
+    assert check_q8(lib, _q8_args(N=0), empty) == sel.DS_SEL_OK
+
+
+@pytest.mark.parametrize("field,value", [
+    ("codes", None), ("codes", 0xB0004),         # missing, or not 8-byte aligned
+    ("scales", None), ("scales", 0xC0001),       # missing, or not 2-byte aligned
+    ("ldc", 120), ("ldc", 132),                  # ldc < d, or not a multiple of 8
+    ("code_layer_stride", 8), ("code_layer_stride", 75000 * 128 + 4),
+    ("lds", 3),                                  # fewer than d/32 scales per row
+    ("scale_layer_stride", 10),                  # layers overlap
+    ("struct_size", 8), ("reserved", 1),
+])
+def test_q8_bad_keys_rejected(lib, field, value):
+    k8 = _q8()
+    setattr(k8, field, value)
+    assert check_q8(lib, _q8_args(), k8) == sel.DS_SEL_E_INVALID
+
+
+def test_q8_rejects_bf16_keys_and_missing_stream(lib):
+    a = _q8_args()
+    a.keys = 0x20000  # the keys come from the 8-bit stream only
+    assert check_q8(lib, a, _q8()) == sel.DS_SEL_E_INVALID
+    assert check_q8(lib, _q8_args(), None) == sel.DS_SEL_E_INVALID
+    assert lib.ds_sel_score_select_q8(None, ctypes.byref(_q8_args()), ctypes.byref(_q8()),
+                                      None) == sel.DS_SEL_E_INVALID
+
+
+def _quant_args(L=2, N=1000, d=128, ldk=None, ldc=None, lds=None):
+    ldk, ldc, lds = ldk or d, ldc or d, lds or d // 32
+    a = sel.QuantizeArgs()
+    a.struct_size = ctypes.sizeof(sel.QuantizeArgs)
+    a.layers, a.dim, a.reserved, a.blocks = L, d, 0, N
+    a.keys, a.ldk, a.key_layer_stride = 0x20000, ldk, N * ldk
+    a.codes, a.ldc, a.code_layer_stride = 0xB0000, ldc, N * ldc
+    a.scales, a.lds, a.scale_layer_stride = 0xC0002, lds, N * lds
+    return a
+
+
+@pytest.mark.parametrize("field,value", [
+    ("layers", 0), ("blocks", -1), ("dim", 96), ("dim", 16), ("reserved", 1), ("struct_size", 4),
+    ("keys", None), ("keys", 0x20008), ("ldk", 120), ("ldk", 132),
+    ("codes", None), ("codes", 0xB0008),         # code rows are written with 16-byte stores
+    ("ldc", 136), ("code_layer_stride", 1000 * 128 - 16),
+    ("scales", 0xC0001), ("lds", 3), ("scale_layer_stride", 3999),
+])
+def test_quantize_bad_arguments_rejected(lib, field, value):
+    a = _quant_args()
+    setattr(a, field, value)
+    assert lib.ds_sel_quantize_q8(ctypes.byref(a), None) == sel.DS_SEL_E_INVALID
+
+
+def test_quantize_checks_before_touching_a_device(lib):
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU driver is present on this host")
+    assert lib.ds_sel_quantize_q8(ctypes.byref(_quant_args()), None) == sel.DS_SEL_E_NODEVICE

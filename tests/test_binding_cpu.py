@@ -147,3 +147,73 @@ def test_accepts_every_gpu_test_shape():
         qa = torch.zeros(p.layers, p.rows, 2, p.dim, dtype=BF)
         idx = torch.zeros(p.layers, p.rows, p.k, dtype=torch.int32)
         sel.check_attend_tensors(qa, keys, keys, idx, None, 0.5, None, CPU)
+
+
+# ------------------------------------------------------------ the 8-bit key stream
+def q8_good():
+    return dict(codes=torch.zeros(L, N, D, dtype=torch.int8),
+                scales=torch.zeros(L, N, D // 32, dtype=torch.float16))
+
+
+def check_q8(**kw):
+    a, s = good(), q8_good()
+    s.update(kw)
+    sel.check_select_q8_tensors(a["q"], a["w"], s["codes"], s["scales"], a["k"], a["mask"], a["limit"],
+                                a["out"], CPU)
+
+
+def test_q8_accepts_well_formed():
+    check_q8()
+    check_q8(codes=torch.zeros(L, N, 72, dtype=torch.int8)[:, :, :D],
+             scales=torch.zeros(L, N, 3, dtype=torch.float16)[:, :, :2])
+    check_q8(codes=torch.zeros(L, 0, D, dtype=torch.int8),
+             scales=torch.zeros(L, 0, D // 32, dtype=torch.float16), )
+
+
+@pytest.mark.parametrize("name,value", [
+    ("codes", torch.zeros(L, N, D, dtype=torch.uint8)),
+    ("codes", torch.zeros(L, N, D, dtype=torch.int16)),
+    ("codes", torch.zeros(L + 1, N, D, dtype=torch.int8)),
+    ("codes", torch.zeros(L, N, D - 8, dtype=torch.int8)),              # rows shorter than d
+    ("codes", torch.zeros(L, N, 2 * D, dtype=torch.int8)[:, :, ::2]),    # non-unit last stride
+    ("scales", torch.zeros(L, N, D // 32)),                              # fp32, not fp16
+    ("scales", torch.zeros(L, N, D // 32, dtype=BF)),
+    ("scales", torch.zeros(L, N + 1, D // 32, dtype=torch.float16)),     # block counts differ
+    ("scales", torch.zeros(L, N, D // 32 - 1, dtype=torch.float16)),     # fewer than d/32
+])
+def test_q8_rejects(name, value):
+    with pytest.raises(ValueError):
+        check_q8(**{name: value})
+
+
+def test_quantize_rejects_before_the_library():
+    with pytest.raises(ValueError):
+        sel.quantize_q8(torch.zeros(L, N, D))                            # fp32 keys
+    with pytest.raises(ValueError):
+        sel.quantize_q8(torch.zeros(L, N, D, dtype=BF), codes=torch.zeros(L, N + 1, D, dtype=torch.int8))
+    with pytest.raises(ValueError):
+        sel.quantize_q8(torch.zeros(L, N, D, dtype=BF),
+                        scales=torch.zeros(L, N, D // 32, dtype=torch.float16, device="meta"))
+
+
+def test_q8_accepts_every_gpu_test_shape():
+    """The 8-bit GPU tests' problems pass both the binding's checks and the C
+    ABI's (ds_sel_check_args_q8 with the tests' handle capacity)."""
+    import ctypes
+    import numpy as np
+    from tests import test_gpu_q8 as tq
+    lib = sel.load_library()
+    lim = sel.make_limits(43, 8, 64, 256, 75000, 2048)
+    for i, c in enumerate(tq.EXACT):
+        p, codes, scales = tq._exact_case(600 + i, *c["args"], exps=c.get("exps", (-3, 0)),
+                                          **c.get("kw", {}))
+        q, w, _, mask, limit = sel.upload(p, "cpu")
+        ct = torch.from_numpy(codes)
+        st = torch.from_numpy(scales.view(np.float16))
+        out = (torch.empty(p.layers, p.rows, p.k, dtype=torch.int32), torch.empty(p.layers, p.rows, p.k),
+               torch.empty(p.layers, p.rows, dtype=torch.int32))
+        sel.check_select_q8_tensors(q, w, ct, st, p.k, mask, limit, out, CPU)
+        a = sel.make_args(q, w, None, p.k, mask, limit, *out, blocks=p.blocks)
+        k8 = sel.make_q8_keys(ct, st)
+        rc = lib.ds_sel_check_args_q8(ctypes.byref(lim), ctypes.byref(a), ctypes.byref(k8))
+        assert rc == sel.DS_SEL_OK, (c["name"], rc)
