@@ -29,7 +29,10 @@ Prints one JSON line on stdout.  Besides the contract's keys it carries:
   cpu_baseline   the oracle timed on one host core on whole selections of the
                  workload (outputs compared with the GPU's), with the host's CPU
                  model and core count;
-  attend         attention over the last step's selection (not part of value).
+  attend         attention over the last step's selection (not part of value);
+  q8             the same workload with the keys as the 8-bit stream (int8
+                 codes, one fp16 scale per 32): throughput and its own
+                 roofline on that stream's algorithmic bytes (not part of value).
 """
 from __future__ import annotations
 
@@ -79,6 +82,7 @@ def parse():
     ap.add_argument("--no-attend", action="store_true", help="skip the attention leg")
     ap.add_argument("--no-singles", action="store_true", help="skip the single-call legs")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the calibration launches")
+    ap.add_argument("--no-q8", action="store_true", help="skip the 8-bit key stream leg")
     ap.add_argument("--calls", type=int, default=200,
                     help="event-bracketed calls per single-call leg")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -144,12 +148,14 @@ def admitted_counts(p):
     return per_row, ubits
 
 
-def algorithmic_bytes(p, union_count):
+def algorithmic_bytes(p, union_count, fmt="bf16"):
     """Bytes the method itself must move per call (intermediates excluded): the
-    union-admitted key rows (2d bytes each, read once for all rows), the mask,
-    q and w, the limits and the outputs."""
+    union-admitted key rows (read once for all rows: 2d bytes each in bf16,
+    d codes + d/32 fp16 scales on the 8-bit stream), the mask, q and w, the
+    limits and the outputs."""
     import numpy as np
-    keys = int(union_count) * 2 * p.dim
+    row = 2 * p.dim if fmt == "bf16" else p.dim + 2 * (p.dim // 32)
+    keys = int(union_count) * row
     mask = 0 if p.mask is None else int(np.prod(p.mask.shape)) * 4
     qw = p.layers * p.rows * p.heads * (p.dim + 1) * 2
     lim = 0 if p.limit is None else p.layers * p.rows * 4
@@ -179,18 +185,25 @@ def pct(xs):
 class Runner:
     """One workload on the device: rotated input copies, outputs, a handle."""
 
-    def __init__(self, p, engine, stream, sets=None):
+    def __init__(self, p, engine, stream, sets=None, fmt="bf16"):
         import numpy as np
         import torch
         from sparse_attention_block_ds_amd import selector as sel
         self.p = p
         self.stream = stream
+        self.fmt = fmt
         self.per_row, self.ubits = admitted_counts(p)
-        self.alg = algorithmic_bytes(p, self.ubits.sum())
+        self.alg = algorithmic_bytes(p, self.ubits.sum(), fmt)
         n = max(2, math.ceil(COLD_BYTES / self.alg["total"])) if sets is None else sets
         first = sel.upload(p, "cuda:0")
-        self.sets = [first] + [tuple(None if t is None else t.clone() for t in first)
-                               for _ in range(n - 1)]
+        if fmt == "q8":  # the keys become the 8-bit stream, made by the quantise kernel
+            q, w, keys, mask, limit = first
+            first = (q, w, sel.quantize_q8(keys, stream=stream), mask, limit)
+            del keys
+            torch.cuda.synchronize()
+        clone = lambda t: None if t is None else (tuple(x.clone() for x in t) if isinstance(t, tuple)
+                                                  else t.clone())
+        self.sets = [first] + [tuple(clone(t) for t in first) for _ in range(n - 1)]
         self.n_sets = n
         self.selector = sel.Selector(max_layers=p.layers, max_rows=p.rows, max_heads=p.heads,
                                      max_dim=p.dim, max_blocks=p.blocks, max_k=p.k, device=0,
@@ -205,8 +218,14 @@ class Runner:
 
     def step(self, i, events=None):
         q, w, keys, mask, limit = self.sets[i % self.n_sets]
-        self.selector.score_select(q, w, keys, self.p.k, mask, limit, out=self.outs[i % self.n_sets],
-                                   stream=self.stream, events=events)
+        if self.fmt == "q8":
+            self.selector.score_select_q8(q, w, keys[0], keys[1], self.p.k, mask, limit,
+                                          out=self.outs[i % self.n_sets], stream=self.stream,
+                                          events=events)
+        else:
+            self.selector.score_select(q, w, keys, self.p.k, mask, limit,
+                                       out=self.outs[i % self.n_sets], stream=self.stream,
+                                       events=events)
 
     def output(self, i):
         return tuple(t.cpu().numpy() for t in self.outs[i % self.n_sets])
@@ -262,16 +281,18 @@ def _sub_problem(p, l, r):
                       None if p.limit is None else p.limit[l:l + 1, r:r + 1])
 
 
-def _accept(p, sub, out, l, r, ora, lib):
-    """The acceptance rule for one (layer, row): bit-exact on integer inputs;
-    otherwise count exact, every returned score within 1e-6 + 1e-5 |oracle
-    score of that block|, and every selected block's oracle score >= oracle
-    m-th score - 1e-4 max |score|."""
+def _accept(p, sub, out, l, r, ora, lib, scorer=None):
+    """The acceptance rule for one (layer, row): bit-exact on integer inputs
+    (bf16 keys); otherwise count exact, every returned score within 1e-6 +
+    1e-5 |oracle score of that block|, and every selected block's oracle score
+    >= oracle m-th score - 1e-4 max |score|.  `scorer(blocks)` gives the
+    oracle's per-block scores when the keys are not sub.keys (the 8-bit
+    stream, always under the general rule)."""
     import numpy as np
     import oracle
     g_idx, g_score, g_count = out
     o_idx, o_score, o_count = ora
-    if p.integer_valued:
+    if p.integer_valued and scorer is None:
         return (np.array_equal(o_idx[0, 0], g_idx[l, r]) and
                 np.array_equal(o_score[0, 0], g_score[l, r]) and o_count[0, 0] == g_count[l, r])
     m = int(o_count[0, 0])
@@ -279,7 +300,10 @@ def _accept(p, sub, out, l, r, ora, lib):
         return False
     if m == 0:
         return True
-    s_or = oracle.score_blocks(sub.q, sub.w, sub.keys, 0, 0, g_idx[l, r, :m], lib=lib)
+    if scorer is None:
+        s_or = oracle.score_blocks(sub.q, sub.w, sub.keys, 0, 0, g_idx[l, r, :m], lib=lib)
+    else:
+        s_or = scorer(g_idx[l, r, :m])
     kth = float(o_score[0, 0, m - 1])
     maxabs = max(abs(float(o_score[0, 0, 0])), abs(kth))
     return (bool(np.all(np.abs(g_score[l, r, :m] - s_or) <= 1e-6 + 1e-5 * np.abs(s_or))) and
@@ -425,6 +449,63 @@ def single_leg(name, engine, stream, calls):
     }
 
 
+def q8_leg(p, stream, steps, warmup):
+    """The same workload on the 8-bit key stream (ds_sel_score_select_q8 over
+    codes and scales made by the quantise kernel): back-to-back throughput,
+    per-call and per-kernel device times, the chain's and the score kernel's
+    fraction of the HBM peak on the stream's algorithmic bytes; the stream of
+    sampled layers is checked bit for bit against the oracle's quantiser and
+    sampled (layer, row) selections against the oracle's 8-bit selection
+    (tolerance + set rule: 8-bit scores are not exact)."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    run = Runner(p, "mfma", stream, fmt="q8")
+    log(f"[bench] q8 leg: {run.n_sets} input copies, quantised in {time.perf_counter() - t0:.1f}s")
+    wall_ms, dev_ms = time_back_to_back(run, steps, warmup)
+    call_us, kernels = per_call(run, steps)
+    out = run.output(steps - 1)
+    codes_d, scales_d = run.sets[(steps - 1) % run.n_sets][2]
+    lib = oracle.load()
+    layers = sorted({0, p.layers // 2, p.layers - 1})
+    pairs = [(l, r) for l in layers for r in sorted({0, p.rows - 1})]
+    bad = 0
+    for l in layers:
+        c_o, s_o = oracle.quantize_q8(p.keys[l:l + 1], lib=lib)
+        c_g = codes_d[l:l + 1].cpu().numpy()
+        s_g = scales_d[l:l + 1].cpu().numpy().view(np.uint16)
+        if not (np.array_equal(c_o, c_g) and np.array_equal(s_o, s_g)):
+            log(f"[bench] PARITY FAILURE in the q8 leg: layer {l}'s 8-bit stream differs")
+            sys.exit(3)
+        for r in sorted({0, p.rows - 1}):
+            sub = _sub_problem(p, l, r)
+            ora = oracle.select_q8(sub.q, sub.w, c_o, s_o, sub.k, sub.mask, sub.limit, lib=lib)
+            scorer = lambda blocks: oracle.score_blocks_q8(sub.q, sub.w, c_o, s_o, 0, 0, blocks, lib=lib)
+            bad += 0 if _accept(p, sub, out, l, r, ora, lib, scorer=scorer) else 1
+    candidates, alg, n_sets = run.candidates, run.alg, run.n_sets
+    run.close()
+    if bad:
+        log(f"[bench] PARITY FAILURE in the q8 leg: {bad} of {len(pairs)} pairs")
+        sys.exit(3)
+    achieved = alg["total"] / (dev_ms * 1e-3) / 1e9
+    score_gbs = alg["keys"] / (kernels["score"] * 1e-6) / 1e9
+    return {
+        "workload": WORKLOADS[p.name] + ", keys as the 8-bit stream (int8 codes, fp16 scale per 32)",
+        "input_copies": n_sets, "ms_per_step": wall_ms, "device_ms_per_step": dev_ms,
+        "candidate_blocks_per_s": candidates / (wall_ms * 1e-3),
+        "device_us_per_call": call_us, "kernels_us_median": kernels,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": alg["total"],
+                     "bytes_per_key_row": p.dim + 2 * (p.dim // 32),
+                     "score_kernel": {"algorithmic_key_bytes": alg["keys"],
+                                      "us_median": kernels["score"], "gbs": score_gbs,
+                                      "frac": score_gbs / HBM_PEAK_GBS}},
+        "parity": f"8-bit stream of layers {layers} bit-exact vs the oracle's quantiser; "
+                  f"{len(pairs)} (layer,row) pairs vs the oracle's 8-bit selection "
+                  "(tolerance + set rule)",
+    }
+
+
 def attend_leg(run, steps):
     """Attention over the last step's selection (64 query heads per row, bf16 q
     and values drawn on the device from a fixed seed), timed with HIP events on
@@ -549,6 +630,13 @@ def main():
             log(f"[bench] {name}: {json.dumps(singles[name]['device_us_per_call'])} us per call")
             torch.cuda.empty_cache()
 
+    q8 = None
+    if not args.no_q8 and p.dim % 32 == 0:
+        q8 = q8_leg(p, stream, args.steps, args.warmup)
+        log(f"[bench] q8 leg: {q8['ms_per_step']:.4f} ms per step, chain "
+            f"{q8['roofline']['frac']:.3f} of the HBM peak")
+        torch.cuda.empty_cache()
+
     traffic = load_traffic(p.name)
     line = {
         "metric": METRIC,
@@ -587,6 +675,7 @@ def main():
         "parity": parity,
         "single_calls": singles,
         "attend": attend,
+        "q8": q8,
     }
     print(json.dumps(line), flush=True)
 

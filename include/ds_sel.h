@@ -71,7 +71,8 @@ enum {
 #define DS_SEL_MAX_BLOCKS (1LL << 26)
 
 /* Create-time flags.  The default key-stream engine feeds the bf16 keys to the
- * matrix cores (the fp32 folded query enters as three exact bf16 parts);
+ * matrix cores (the fp32 folded query enters as three bf16 parts, whose sum
+ * is the query exactly for |q~_i| >= 2^-110 and within 2^-133 below that);
  * DS_SEL_FLAG_VALU_SCORE selects fp32 FMAs on the vector ALUs instead.  Both
  * return the same selection on integer-valued inputs; on general inputs their
  * scores differ only by fp32 rounding order. */
@@ -189,9 +190,11 @@ typedef struct {
 
 /* ds_sel_score_select over the 8-bit key stream `k8`; a->keys must be NULL
  * (the keys come from k8), everything else of `a` and every rule of
- * ds_sel_score_select (handle, stream, status codes) applies unchanged. */
+ * ds_sel_score_select (handle, stream, status codes) applies unchanged.
+ * `events` is NULL, or four hipEvent_t recorded as ds_sel_score_select_profiled
+ * records them. */
 int ds_sel_score_select_q8(ds_sel* h, const ds_sel_args* a, const ds_sel_q8_keys* k8,
-                           void* hip_stream);
+                           void* hip_stream, void* const events[4]);
 
 /* The host-side checks ds_sel_score_select_q8 applies, without a device. */
 int ds_sel_check_args_q8(const ds_sel_limits* lim, const ds_sel_args* a, const ds_sel_q8_keys* k8);
@@ -310,6 +313,13 @@ typedef struct {
 } ds_sel_calib_args;
 
 int ds_sel_calibrate(const ds_sel_calib_args* a, void* hip_stream);
+
+/* Fill every byte of the handle's scratch with `byte` (0..255), enqueued on
+ * `hip_stream` like a call.  For tests that check that no call depends on
+ * what an earlier call left in the scratch; it uses hipMemsetAsync, so keep it
+ * out of captured graphs.  DS_SEL_E_INVALID for a NULL handle or a byte out
+ * of range. */
+int ds_sel_poison_scratch(ds_sel* h, int32_t byte, void* hip_stream);
 
 /* Free the handle and its scratch, after waiting for the handle's last
  * enqueued call to finish (only that work: other streams and handles are not

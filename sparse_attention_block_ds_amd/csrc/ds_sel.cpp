@@ -365,11 +365,22 @@ int ds_sel_score_select_profiled(ds_sel* h, const ds_sel_args* a, void* hip_stre
   return enqueue(handle_target(h), a, hip_stream, events);
 }
 
-int ds_sel_score_select_q8(ds_sel* h, const ds_sel_args* a, const ds_sel_q8_keys* k8, void* hip_stream) {
+int ds_sel_poison_scratch(ds_sel* h, int32_t byte, void* hip_stream) {
+  if (!h || byte < 0 || byte > 255) return DS_SEL_E_INVALID;
+  return with_device(h->lim.device, [&]() {
+    const hipError_t e = hipMemsetAsync(h->scratch, byte, (size_t)h->lay.total,
+                                        static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return (int)DS_SEL_E_HIP;
+    return mark_done(h->done, static_cast<hipStream_t>(hip_stream));
+  });
+}
+
+int ds_sel_score_select_q8(ds_sel* h, const ds_sel_args* a, const ds_sel_q8_keys* k8, void* hip_stream,
+                           void* const events[4]) {
   if (!h || !k8) return DS_SEL_E_INVALID;
   const int rc = check_args(h->lim, a, k8);
   if (rc != DS_SEL_OK) return rc;
-  return enqueue(handle_target(h), a, hip_stream, nullptr, k8);
+  return enqueue(handle_target(h), a, hip_stream, events, k8);
 }
 
 int ds_sel_check_args_q8(const ds_sel_limits* lim, const ds_sel_args* a, const ds_sel_q8_keys* k8) {

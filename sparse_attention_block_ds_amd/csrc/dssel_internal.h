@@ -51,7 +51,7 @@ enum KeyFormat : int {
 };
 
 enum Engine : int {
-  kEngineMfma = 0,  // bf16 matrix cores on an exact 3-way bf16 split of the fp32 q~
+  kEngineMfma = 0,  // bf16 matrix cores on a 3-way bf16 split of the fp32 q~ (exact for |q~_i| >= 2^-110)
   kEngineValu = 1,  // fp32 FMAs on the vector ALUs
 };
 

@@ -20,8 +20,11 @@
 // (sum_h w_h q_h) . K_b, so each row's H query heads collapse into one fp32
 // vector q~ before the key stream (the products w_h q_hi are bf16 x bf16 and
 // exact in fp32; the sum runs in ascending h).  For the matrix cores q~ is
-// also split exactly into three bf16 parts, hi = bf16(q~), mid = bf16(q~ - hi),
-// lo = bf16(q~ - hi - mid), with hi + mid + lo == q~.
+// also split into three bf16 parts, hi = bf16(q~), mid = bf16(q~ - hi),
+// lo = bf16(q~ - hi - mid), with hi + mid + lo == q~ exactly whenever
+// |q~_i| >= 2^-110 (the lowest of q~'s 24 bits is then at or above bf16's
+// least subnormal 2^-133); below that lo drops bits and the parts sum to q~
+// within 2^-133, far below any score tolerance.
 //
 // Candidate floors (workgroup 0): the key stream writes only keys that can
 // still be among a row's best k, i.e. keys at or above the row's floor.  The
@@ -430,7 +433,7 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
   }
 
   // fold, second half: the slices' partial sums in ascending slice order; the
-  // exact three-way bf16 split
+  // three-way bf16 split (exact for |q~_i| >= 2^-110)
   for (int o = tid; o < R * D; o += kPrepThreads) {
     const int r = o / D, i = o % D;
     const int64_t lr = (int64_t)l * R + r;

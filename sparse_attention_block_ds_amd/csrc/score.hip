@@ -21,7 +21,8 @@
 //     and loads their K rows with 16-byte loads (each instruction reads 16 rows
 //     x 64 contiguous bytes), two steps ahead of the arithmetic.
 //       MFMA engine: v_mfma_f32_16x16x32_bf16 with the fp32 q~ entering as
-//       three exact bf16 parts (hi + mid + lo == q~) along the M dimension
+//       three bf16 parts (hi + mid + lo == q~, exact for |q~_i| >= 2^-110)
+//       along the M dimension
 //       (row m = 4 * (query row % 4) + part), so the bf16 keys feed the
 //       matrix cores directly: no vector-ALU conversion, no cross-lane sum.
 //       VALU engine: d/8 lanes per key row, 8 fp32 FMAs per lane and row, a
@@ -264,7 +265,7 @@ struct MfmaEngine {
 };
 
 // ------------------------------------------------------- MFMA engine, 8-bit keys
-// The same A operand (q~ as three exact bf16 parts along M) against 8-bit key
+// The same A operand (q~ as three bf16 parts along M) against 8-bit key
 // rows: group g of a row is 32 int8 codes c with one fp16 scale s, standing
 // for the values s c.  Each 32-column chunk is one group, so each chunk gets
 // its own accumulation: the codes widen exactly to bf16 (B operand), one

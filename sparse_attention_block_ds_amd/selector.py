@@ -28,7 +28,8 @@ EXPORTED = ("ds_sel_create", "ds_sel_score_select", "ds_sel_score_select_profile
             "ds_sel_destroy", "ds_sel_check_args", "ds_sel_scratch_bytes", "ds_sel_status_string",
             "ds_sel_attend", "ds_sel_check_attend_args", "ds_sel_calibrate",
             "ds_sel_score_select_noalloc", "ds_sel_noalloc_scratch_bytes",
-            "ds_sel_score_select_q8", "ds_sel_check_args_q8", "ds_sel_quantize_q8")
+            "ds_sel_score_select_q8", "ds_sel_check_args_q8", "ds_sel_quantize_q8",
+            "ds_sel_poison_scratch")
 
 DS_SEL_CALIB_EMPTY = 0
 DS_SEL_CALIB_READ = 1
@@ -138,12 +139,15 @@ def load_library(path: Optional[str] = None):
     lib.ds_sel_noalloc_scratch_bytes.restype = ctypes.c_int64
     lib.ds_sel_calibrate.argtypes = [P(CalibArgs), ctypes.c_void_p]
     lib.ds_sel_calibrate.restype = ctypes.c_int
-    lib.ds_sel_score_select_q8.argtypes = [ctypes.c_void_p, P(Args), P(Q8Keys), ctypes.c_void_p]
+    lib.ds_sel_score_select_q8.argtypes = [ctypes.c_void_p, P(Args), P(Q8Keys), ctypes.c_void_p,
+                                           ctypes.POINTER(ctypes.c_void_p)]
     lib.ds_sel_score_select_q8.restype = ctypes.c_int
     lib.ds_sel_check_args_q8.argtypes = [P(Limits), P(Args), P(Q8Keys)]
     lib.ds_sel_check_args_q8.restype = ctypes.c_int
     lib.ds_sel_quantize_q8.argtypes = [P(QuantizeArgs), ctypes.c_void_p]
     lib.ds_sel_quantize_q8.restype = ctypes.c_int
+    lib.ds_sel_poison_scratch.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.ds_sel_poison_scratch.restype = ctypes.c_int
     lib.ds_sel_status_string.argtypes = [ctypes.c_int]
     lib.ds_sel_status_string.restype = ctypes.c_char_p
     if default:
@@ -411,11 +415,23 @@ class Selector:
         return out
 
 
+    def poison_scratch(self, byte, stream=None):
+        """Fill the handle's scratch with `byte` (a test hook: results must not
+        depend on what earlier calls left there)."""
+        torch = self._torch
+        if stream is None:
+            stream = torch.cuda.current_stream(torch.device("cuda", self.device))
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        rc = self.lib.ds_sel_poison_scratch(self.handle, int(byte), ctypes.c_void_p(handle))
+        if rc != DS_SEL_OK:
+            raise DsSelError(rc, "ds_sel_poison_scratch")
+
     def score_select_q8(self, q, w, codes, scales, k, mask=None, limit=None, out=None,
-                        stream=None):
+                        stream=None, events=None):
         """score_select over the 8-bit key stream (ds_sel_score_select_q8):
         codes int8 [L,N,ldc] and scales float16 [L,N,lds] as quantize_q8
-        returns them; every other argument and the result as score_select."""
+        returns them; every other argument (events included) and the result
+        as score_select."""
         torch = self._torch
         dev = torch.device("cuda", self.device)
         check_select_q8_tensors(q, w, codes, scales, k, mask, limit, out, dev)
@@ -429,8 +445,14 @@ class Selector:
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        ev = None
+        if events is not None:
+            for e in events:  # torch creates the HIP event on its first record
+                if not e.cuda_event:
+                    e.record(stream)
+            ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
         rc = self.lib.ds_sel_score_select_q8(self.handle, ctypes.byref(a), ctypes.byref(k8),
-                                             ctypes.c_void_p(handle))
+                                             ctypes.c_void_p(handle), ev)
         if rc != DS_SEL_OK:
             raise DsSelError(rc, "ds_sel_score_select_q8")
         return out

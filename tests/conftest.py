@@ -15,5 +15,10 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def oracle_lib():
+    """The oracle; DS_SEL_TEST_ORACLE names another build of it (the sanitizer
+    run), which then also serves every default oracle call."""
     import oracle
+    path = os.environ.get("DS_SEL_TEST_ORACLE")
+    if path:
+        oracle._lib = oracle.load(path)
     return oracle.load()

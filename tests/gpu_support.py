@@ -34,6 +34,27 @@ def run_oracle(p: wl.Problem, k=None):
     return oracle.select(p.q, p.w, p.keys, p.k if k is None else k, p.mask, p.limit)
 
 
+def sub_problem(p: wl.Problem, l, r):
+    """The (layer l, row r) selection of p as a one-layer, one-row problem."""
+    mrow = 0 if p.mask is None or p.mask.shape[1] == 1 else r
+    return wl.Problem(f"{p.name}[{l},{r}]", p.k, p.q[l:l + 1, r:r + 1], p.w[l:l + 1, r:r + 1],
+                      p.keys[l:l + 1], None if p.mask is None else p.mask[l:l + 1, mrow:mrow + 1],
+                      None if p.limit is None else p.limit[l:l + 1, r:r + 1], p.integer_valued)
+
+
+def oracle_pairs(p: wl.Problem, pairs, threads=8):
+    """The oracle's result for each (layer, row) of `pairs`, on a pool of host
+    threads (ctypes releases the GIL while the oracle runs)."""
+    from concurrent.futures import ThreadPoolExecutor
+    lib = oracle.load()
+
+    def one(lr):
+        sub = sub_problem(p, *lr)
+        return oracle.select(sub.q, sub.w, sub.keys, sub.k, sub.mask, sub.limit, lib=lib)
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(one, pairs))
+
+
 def assert_bit_exact(gpu, ora, what=""):
     for name, g, o in zip(("idx", "score", "count"), gpu, ora):
         if not np.array_equal(g, o):

@@ -15,6 +15,10 @@ HEADER = os.path.join(ROOT, "include", "ds_sel.h")
 
 @pytest.fixture(scope="module")
 def lib():
+    """libdssel.so; DS_SEL_TEST_LIBRARY names another build of it (the sanitizer run)."""
+    path = os.environ.get("DS_SEL_TEST_LIBRARY")
+    if path:
+        return sel.load_library(path)
     if not os.path.exists(sel.LIBRARY):
         from sparse_attention_block_ds_amd import build
         build.build(verbose=False)
@@ -214,6 +218,7 @@ def test_no_device_or_create(lib):
 
 def test_destroy_null_is_noop_and_status_strings(lib):
     lib.ds_sel_destroy(None)
+    assert lib.ds_sel_poison_scratch(None, 0xFF, None) == sel.DS_SEL_E_INVALID
     assert lib.ds_sel_status_string(0) == b"ok"
     assert lib.ds_sel_status_string(sel.DS_SEL_E_CAPACITY) == b"exceeds the handle's capacity"
     assert lib.ds_sel_status_string(99) == b"unknown status"
@@ -356,7 +361,7 @@ def test_q8_rejects_bf16_keys_and_missing_stream(lib):
     assert check_q8(lib, a, _q8()) == sel.DS_SEL_E_INVALID
     assert check_q8(lib, _q8_args(), None) == sel.DS_SEL_E_INVALID
     assert lib.ds_sel_score_select_q8(None, ctypes.byref(_q8_args()), ctypes.byref(_q8()),
-                                      None) == sel.DS_SEL_E_INVALID
+                                      None, None) == sel.DS_SEL_E_INVALID
 
 
 def _quant_args(L=2, N=1000, d=128, ldk=None, ldc=None, lds=None):

@@ -49,18 +49,41 @@ def test_general_workloads(selector, name):
     gs.assert_general(p, gpu, gs.run_oracle(p))
 
 
-def test_sweep_full_size_sampled(selector):
-    """All 43 x 6 selections at full size: invariants everywhere, bit-exact on a sample."""
-    p = wl.make("sweep")
+_FULL = {}
+
+
+def _full_size(name):
+    """A full-size workload and the oracle's result for every (layer, row), computed
+    once per module on a pool of host threads (the oracle runs without the GIL)."""
+    if name not in _FULL:
+        p = wl.make(name)
+        pairs = [(l, r) for l in range(p.layers) for r in range(p.rows)]
+        _FULL[name] = (p, dict(zip(pairs, gs.oracle_pairs(p, pairs))))
+    return _FULL[name]
+
+
+def test_sweep_full_size_all_pairs(selector):
+    """All 43 x 6 selections of the sweep at full size, every one bit-exact."""
+    p, ora = _full_size("sweep")
     _print_case("sweep", p)
     gpu = gs.run_gpu(selector, p)
     gs.assert_self_consistent(p, gpu)
-    for l, r in [(0, 0), (0, 5), (17, 3), (42, 0), (42, 5)]:
-        sub = wl.Problem("s", p.k, p.q[l:l + 1, r:r + 1], p.w[l:l + 1, r:r + 1], p.keys[l:l + 1],
-                         p.mask[l:l + 1], p.limit[l:l + 1, r:r + 1])
-        o = gs.run_oracle(sub)
+    for (l, r), o in ora.items():
         got = tuple(x[l:l + 1, r:r + 1] for x in gpu)
         gs.assert_bit_exact(got, o, f"sweep l={l} r={r}")
+
+
+def test_300k_x43_all_layers(selector):
+    """The 300k config batched 43 layers to a call (one row each): every layer
+    against the oracle under the general-input rule."""
+    p, ora = _full_size("300k_x43")
+    _print_case("300k_x43", p)
+    gpu = gs.run_gpu(selector, p)
+    gs.assert_self_consistent(p, gpu)
+    for (l, r), o in ora.items():
+        sub = gs.sub_problem(p, l, r)
+        got = tuple(x[l:l + 1, r:r + 1] for x in gpu)
+        gs.assert_general(sub, got, o)
 
 
 # ------------------------------------------------------------ edge cases (integer: bit-exact)
