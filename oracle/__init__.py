@@ -58,6 +58,10 @@ def _declare(lib):
     lib.ds_sel_oracle_score_blocks.restype = ctypes.c_int
     lib.ds_sel_oracle_score_blocks.argtypes = [i32, i32, i32, i32, i64, p, p, p, i64, i64, i32,
                                                i32, i64, p, p]
+    lib.ds_sel_oracle_select_relu.restype = ctypes.c_int
+    lib.ds_sel_oracle_select_relu.argtypes = lib.ds_sel_oracle_select.argtypes
+    lib.ds_sel_oracle_score_blocks_relu.restype = ctypes.c_int
+    lib.ds_sel_oracle_score_blocks_relu.argtypes = lib.ds_sel_oracle_score_blocks.argtypes
     lib.ds_sel_oracle_attend.restype = ctypes.c_int
     lib.ds_sel_oracle_quantize_q8.restype = ctypes.c_int
     lib.ds_sel_oracle_quantize_q8.argtypes = [i32, i64, i32, p, i64, i64, p, i64, i64, p, i64, i64]
@@ -116,8 +120,11 @@ def _shapes(q, w, keys, mask):
     return layers, rows, heads, dim, blocks, ldk, mrow, mlayer
 
 
-def select(q, w, keys, k, mask=None, limit=None, lib=None):
+def select(q, w, keys, k, mask=None, limit=None, lib=None, score="linear"):
     """Top-k selection for every (layer, row).
+
+    score "linear": sum_h w_h (q_h . K); "relu": sum_h w_h max(q_h . K, 0)
+    (the per-head ReLU variant, ds_sel_oracle_select_relu).
 
     q     uint16 [L][R][H][d]   bf16 bits
     w     uint16 [L][R][H]      bf16 bits
@@ -133,29 +140,37 @@ def select(q, w, keys, k, mask=None, limit=None, lib=None):
     if limit is not None and limit.shape != (layers, rows):
         raise ValueError("limit must be [layers][rows]")
     idx = np.empty((layers, rows, k), np.int32)
-    score = np.empty((layers, rows, k), np.float32)
+    scores = np.empty((layers, rows, k), np.float32)
     count = np.empty((layers, rows), np.int32)
     lib = lib or load()
-    rc = lib.ds_sel_oracle_select(layers, rows, heads, dim, blocks, k, _ptr(q), _ptr(w),
-                                  _ptr(keys), ldk, blocks * ldk, _ptr(mask), mrow, mlayer,
-                                  _ptr(limit), _ptr(idx), _ptr(score), _ptr(count))
+    fn = _scored(lib, "ds_sel_oracle_select", score)
+    rc = fn(layers, rows, heads, dim, blocks, k, _ptr(q), _ptr(w), _ptr(keys), ldk, blocks * ldk,
+            _ptr(mask), mrow, mlayer, _ptr(limit), _ptr(idx), _ptr(scores), _ptr(count))
     if rc != 0:
-        raise OracleError(f"ds_sel_oracle_select returned {rc}")
-    return idx, score, count
+        raise OracleError(f"{fn.__name__} returned {rc}")
+    return idx, scores, count
 
 
-def score_blocks(q, w, keys, layer, row, blocks_list, lib=None):
+def _scored(lib, name, score):
+    if score == "linear":
+        return getattr(lib, name)
+    if score == "relu":
+        return getattr(lib, name + "_relu")
+    raise ValueError("score must be 'linear' or 'relu'")
+
+
+def score_blocks(q, w, keys, layer, row, blocks_list, lib=None, score="linear"):
     """fp32 scores (the oracle's fixed order) of the listed blocks of one (layer, row)."""
     q, w, keys = _c(q, np.uint16), _c(w, np.uint16), _c(keys, np.uint16)
     lst = _c(blocks_list, np.int32)
     layers, rows, heads, dim, blocks, ldk, _, _ = _shapes(q, w, keys, None)
     out = np.empty(lst.shape[0], np.float32)
     lib = lib or load()
-    rc = lib.ds_sel_oracle_score_blocks(layers, rows, heads, dim, blocks, _ptr(q), _ptr(w),
-                                        _ptr(keys), ldk, blocks * ldk, layer, row, lst.shape[0],
-                                        _ptr(lst), _ptr(out))
+    fn = _scored(lib, "ds_sel_oracle_score_blocks", score)
+    rc = fn(layers, rows, heads, dim, blocks, _ptr(q), _ptr(w), _ptr(keys), ldk, blocks * ldk, layer,
+            row, lst.shape[0], _ptr(lst), _ptr(out))
     if rc != 0:
-        raise OracleError(f"ds_sel_oracle_score_blocks returned {rc}")
+        raise OracleError(f"{fn.__name__} returned {rc}")
     return out
 
 

@@ -211,6 +211,113 @@ int ds_sel_oracle_score_blocks(int32_t layers, int32_t rows, int32_t heads, int3
 }
 
 /*
+ * The per-head ReLU score (a non-linear variant).
+ *
+ * The pages give no score formula (page "DeepSeek V4.1F Q4 on M3 Ultra with
+ * native DSpark MTP (40tps / 800tps)", paragraph "Decode at depth": blocks
+ * are scored and the best kept).  This variant clamps each head's dot product
+ * at zero before weighting:
+ *   score(b) = sum over heads h of w[h] * max(q[h] . K[b], 0)
+ * so the heads can no longer be folded into one query vector.  Same fixed
+ * fp32 order as score_fp32():
+ *   s = +0
+ *   for h = 0..H-1:
+ *     dot = +0;  for i = 0..d-1: dot = dot + q[h][i]*K[i]
+ *     r = dot if dot > 0, else +0
+ *     t = w[h]*r;  s = s + t
+ * Admission, order, output and padding are those of ds_sel_oracle_select.
+ */
+static float score_relu_fp32(const uint16_t* q_row, const uint16_t* w_row, const uint16_t* key,
+                             int heads, int dim) {
+  float s = 0.0f;
+  for (int h = 0; h < heads; ++h) {
+    const uint16_t* qh = q_row + (int64_t)h * dim;
+    float dot = 0.0f;
+    for (int i = 0; i < dim; ++i) {
+      float prod = bf16_bits_to_float(qh[i]) * bf16_bits_to_float(key[i]);
+      dot = dot + prod;
+    }
+    float r = dot > 0.0f ? dot : 0.0f;
+    float t = bf16_bits_to_float(w_row[h]) * r;
+    s = s + t;
+  }
+  return s + 0.0f;
+}
+
+/* Top-k selection under the per-head ReLU score; arguments and returns as
+ * ds_sel_oracle_select. */
+int ds_sel_oracle_select_relu(int32_t layers, int32_t rows, int32_t heads, int32_t dim,
+                              int64_t blocks, int32_t k, const uint16_t* q, const uint16_t* w,
+                              const uint16_t* keys, int64_t ldk, int64_t key_layer_stride,
+                              const uint32_t* mask, int64_t mask_row_stride,
+                              int64_t mask_layer_stride, const int32_t* limit, int32_t* out_idx,
+                              float* out_score, int32_t* out_count) {
+  if (layers < 1 || rows < 1 || heads < 1 || dim < 1 || blocks < 0 || k < 1) return ORACLE_E_INVALID;
+  if (ldk < dim || !q || !w || !out_idx || !out_score) return ORACLE_E_INVALID;
+  if (blocks > 0 && !keys) return ORACLE_E_INVALID;
+  if (blocks > 0x7FFFFFFFLL) return ORACLE_E_INVALID;
+  if (!inputs_finite((int64_t)layers * rows * heads, q, dim, dim)) return ORACLE_E_NONFINITE;
+  if (!inputs_finite((int64_t)layers * rows, w, heads, heads)) return ORACLE_E_NONFINITE;
+  for (int32_t l = 0; l < layers; ++l)
+    if (blocks > 0 && !inputs_finite(blocks, keys + l * key_layer_stride, ldk, dim))
+      return ORACLE_E_NONFINITE;
+
+  scored_block* list = NULL;
+  if (blocks > 0) {
+    list = (scored_block*)malloc((size_t)blocks * sizeof *list);
+    if (!list) return ORACLE_E_NOMEM;
+  }
+  for (int32_t l = 0; l < layers; ++l) {
+    const uint16_t* layer_keys = keys ? keys + l * key_layer_stride : NULL;
+    for (int32_t r = 0; r < rows; ++r) {
+      int64_t lr = (int64_t)l * rows + r;
+      const uint16_t* q_row = q + lr * heads * dim;
+      const uint16_t* w_row = w + lr * heads;
+      const uint32_t* mrow = mask ? mask + l * mask_layer_stride + r * mask_row_stride : NULL;
+      int64_t lim = clamped_limit(limit, lr, blocks);
+      int64_t n = 0;
+      for (int64_t b = 0; b < lim; ++b) {
+        if (mrow && !mask_bit(mrow, b)) continue;
+        list[n].block = (int32_t)b;
+        ++n;
+      }
+      for (int64_t j = 0; j < n; ++j)
+        list[j].score = score_relu_fp32(q_row, w_row, layer_keys + (int64_t)list[j].block * ldk,
+                                        heads, dim);
+      if (n > 1) qsort(list, (size_t)n, sizeof *list, by_score_desc_then_index);
+      int64_t m = n < k ? n : k;
+      int32_t* oi = out_idx + lr * k;
+      float* os = out_score + lr * k;
+      for (int64_t j = 0; j < k; ++j) {
+        oi[j] = j < m ? list[j].block : -1;
+        os[j] = j < m ? list[j].score : -INFINITY;
+      }
+      if (out_count) out_count[lr] = (int32_t)m;
+    }
+  }
+  free(list);
+  return ORACLE_OK;
+}
+
+/* The per-head ReLU score of each listed block for one (layer, row), as
+ * ds_sel_oracle_score_blocks. */
+int ds_sel_oracle_score_blocks_relu(int32_t layers, int32_t rows, int32_t heads, int32_t dim,
+                                    int64_t blocks, const uint16_t* q, const uint16_t* w,
+                                    const uint16_t* keys, int64_t ldk, int64_t key_layer_stride,
+                                    int32_t layer, int32_t row, int64_t n_list, const int32_t* list,
+                                    float* out) {
+  if (layer < 0 || layer >= layers || row < 0 || row >= rows || n_list < 0) return ORACLE_E_INVALID;
+  if (heads < 1 || dim < 1 || ldk < dim) return ORACLE_E_INVALID;
+  int64_t lr = (int64_t)layer * rows + row;
+  for (int64_t j = 0; j < n_list; ++j) {
+    if (list[j] < 0 || list[j] >= blocks) return ORACLE_E_INVALID;
+    out[j] = score_relu_fp32(q + lr * heads * dim, w + lr * heads,
+                             keys + layer * key_layer_stride + (int64_t)list[j] * ldk, heads, dim);
+  }
+  return ORACLE_OK;
+}
+
+/*
  * The 8-bit compressed-key stream.
  *
  * Page "DeepSeek V4.1F Q4 on M3 Ultra with native DSpark MTP (40tps /

@@ -360,6 +360,92 @@ def check_select_q8(lib):
             np.testing.assert_array_equal(got, np.array([by[b] for b in np.sort(blk).tolist()], np.float32))
 
 
+# ------------------------------------------------------------------ per-head ReLU score
+def exact_int_relu_scores(p: wl.Problem) -> np.ndarray:
+    """int64 [L][R][N] per-head ReLU scores of integer-valued inputs, exactly:
+    each head's dot product in int64, clamped at 0, weighted, summed."""
+    q = wl.bf16_bits_to_f32(p.q).astype(np.int64)
+    w = wl.bf16_bits_to_f32(p.w).astype(np.int64)
+    keys = wl.bf16_bits_to_f32(p.keys[:, :, :p.dim]).astype(np.int64)
+    assert np.all(q == wl.bf16_bits_to_f32(p.q)), "inputs must be integer-valued"
+    dots = np.einsum("lrhd,lnd->lrhn", q, keys)        # per head, not folded
+    return np.einsum("lrh,lrhn->lrn", w, np.maximum(dots, 0))
+
+
+def _relu(p, lib, k=None):
+    return oracle.select(p.q, p.w, p.keys, p.k if k is None else k, p.mask, p.limit, lib=lib,
+                         score="relu")
+
+
+def check_select_relu(lib):
+    """The per-head ReLU variant against facts independent of its code."""
+    # 1. integer inputs with negative weights and negative head dots: every
+    #    output exact against int64 per-head arithmetic and a brute-force rank
+    for p in (wl.make_custom(2, 3, 8, 64, 900, 200, seed=90, values="int3", mask_p=0.6,
+                             mask_shared=False, limits=np.array([[900, 450, 17]] * 2)),
+              wl.make_custom(1, 6, 16, 128, 700, 700, seed=91, values="ternary")):
+        exact = exact_int_relu_scores(p)
+        assert np.abs(exact).max() < 2 ** 24
+        idx, score, count = _relu(p, lib)
+        adm = admitted_mask(p)
+        for l in range(p.layers):
+            for r in range(p.rows):
+                e_idx, e_val, e_cnt = brute_force_topk(exact[l, r], adm[l, r], p.k)
+                assert count[l, r] == e_cnt
+                np.testing.assert_array_equal(idx[l, r], e_idx)
+                np.testing.assert_array_equal(score[l, r], e_val.astype(np.float32))
+    # the integer case above must exercise both signs of w and of the head dots
+    p = wl.make_custom(1, 1, 8, 64, 300, 10, seed=92, values="int3")
+    q = wl.bf16_bits_to_f32(p.q).astype(np.int64)
+    dots = np.einsum("lrhd,lnd->lrhn", q, wl.bf16_bits_to_f32(p.keys).astype(np.int64))
+    assert (dots < 0).any() and (dots > 0).any() and (wl.bf16_bits_to_f32(p.w) < 0).any()
+    # 2. general inputs, k >= N: within the fp32 bound of fp64 (ReLU is 1-Lipschitz,
+    #    so the linear score's bound 2 gamma_(d+H) sum_h |w_h| sum_i |q_hi K_bi| holds)
+    p = wl.make_custom(2, 2, 32, 128, 500, 500, seed=93, values="normal", mask_p=0.7)
+    idx, score, count = _relu(p, lib, k=p.blocks)
+    qf = wl.bf16_bits_to_f32(p.q).astype(np.float64)
+    wf = wl.bf16_bits_to_f32(p.w).astype(np.float64)
+    kf = wl.bf16_bits_to_f32(p.keys).astype(np.float64)
+    adm = admitted_mask(p)
+    for l in range(2):
+        for r in range(2):
+            n = int(adm[l, r].sum())
+            assert count[l, r] == n
+            blk = idx[l, r, :n]
+            assert np.array_equal(np.sort(blk), np.flatnonzero(adm[l, r]))
+            s64 = wf[l, r] @ np.maximum(qf[l, r] @ kf[l][blk].T, 0.0)
+            mag = np.abs(wf[l, r]) @ (np.abs(qf[l, r]) @ np.abs(kf[l][blk]).T)
+            assert np.all(np.abs(score[l, r, :n] - s64) <= 2 * gamma(128 + 32) * mag + 1e-30)
+            # 5. the per-block scorer equals the selection's scores, bit for bit
+            got = oracle.score_blocks(p.q, p.w, p.keys, l, r, np.sort(blk), lib=lib, score="relu")
+            by = dict(zip(blk.tolist(), score[l, r, :n].tolist()))
+            np.testing.assert_array_equal(got, np.array([by[b] for b in np.sort(blk).tolist()],
+                                                        np.float32))
+    # 3. every head dot >= 0 (q, K >= 0): identical bits to the linear score
+    rng = np.random.default_rng(94)
+    L, R, H, d, N = 1, 3, 16, 64, 400
+    qpos = wl.f32_to_bf16_bits(np.abs(rng.standard_normal((L, R, H, d))).astype(np.float32))
+    kpos = wl.f32_to_bf16_bits(np.abs(rng.standard_normal((L, N, d))).astype(np.float32))
+    wgen = wl.f32_to_bf16_bits(rng.standard_normal((L, R, H)).astype(np.float32))
+    a = oracle.select(qpos, wgen, kpos, 100, lib=lib, score="relu")
+    b = oracle.select(qpos, wgen, kpos, 100, lib=lib)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    # 4. every head dot <= 0 (q >= 0, K <= 0): all scores +0, the first k admitted
+    kneg = wl.f32_to_bf16_bits(-np.abs(rng.standard_normal((L, N, d))).astype(np.float32))
+    idx, score, count = oracle.select(qpos, wgen, kneg, 50, lib=lib, score="relu")
+    assert np.all(idx == np.arange(50)[None, None, :]) and np.all(count == 50)
+    assert np.all(score == 0.0) and not np.signbit(score).any()
+    # 6. one head with weight 1: score = max(linear score, 0), bit for bit
+    q1, w1 = qpos[:, :, :1].copy(), np.full((L, R, 1), 0x3F80, np.uint16)
+    kmix = wl.f32_to_bf16_bits(rng.standard_normal((L, N, d)).astype(np.float32))
+    all_b = np.arange(N)
+    for r in range(R):
+        lin = oracle.score_blocks(qpos[:, :, :1].copy(), w1, kmix, 0, r, all_b, lib=lib)
+        rel = oracle.score_blocks(q1, w1, kmix, 0, r, all_b, lib=lib, score="relu")
+        np.testing.assert_array_equal(rel, np.where(lin > 0, lin, np.float32(0.0)))
+
+
 # ------------------------------------------------------------------ attention
 def _bits(a):
     return wl.f32_to_bf16_bits(np.asarray(a, np.float32))
@@ -470,6 +556,7 @@ def all_pins(lib, include_slow=False):
     check_score_blocks(lib)
     check_quantize_q8(lib)
     check_select_q8(lib)
+    check_select_relu(lib)
     check_attend(lib)
     if include_slow:
         check_exact_integer(wl.make("tiny"), lib)
