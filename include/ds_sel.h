@@ -78,6 +78,19 @@ enum {
  * scores differ only by fp32 rounding order. */
 #define DS_SEL_FLAG_VALU_SCORE 1u
 
+/* The per-head ReLU score, a non-linear variant of the block score (the pages
+ * give no formula: page "DeepSeek V4.1F Q4 on M3 Ultra with native DSpark MTP
+ * (40tps / 800tps)", paragraph "Decode at depth"):
+ *   score(b) = sum_h w[h] * max(q[h] . K[b], 0)     bf16 inputs, fp32 sums
+ * The heads no longer fold into one query vector, so every (row, head) pair
+ * meets every admitted key on the matrix cores (R x H x d multiply-adds per
+ * block).  Admission, order, output and padding are unchanged.  A handle
+ * created with this flag scores every call this way.  Supported with bf16
+ * keys and the default engine, when one layer's heads fit the kernel's LDS
+ * stage: R * ceil16(H) * (2 (d + 8) + 4) bytes <= 122,864 (e.g. R <= 6 at
+ * H = 64, d = 128); otherwise a call returns DS_SEL_E_UNSUPPORTED. */
+#define DS_SEL_FLAG_HEAD_RELU 2u
+
 typedef struct ds_sel ds_sel; /* opaque handle; owns device scratch */
 
 /* Create-time capacity.  Every call on the handle must fit inside it. */

@@ -66,6 +66,8 @@ struct ds_sel {
 
 namespace {
 
+constexpr int32_t kKnownFlags = DS_SEL_FLAG_VALU_SCORE | DS_SEL_FLAG_HEAD_RELU;
+
 int check_limits(const ds_sel_limits* lim) {
   if (!lim || lim->struct_size != sizeof(ds_sel_limits)) return DS_SEL_E_INVALID;
   if (lim->max_layers < 1 || lim->max_layers > 65535) return DS_SEL_E_INVALID;
@@ -74,7 +76,7 @@ int check_limits(const ds_sel_limits* lim) {
   if (lim->max_dim < 1 || lim->max_dim > DS_SEL_MAX_DIM) return DS_SEL_E_INVALID;
   if (lim->max_k < 1 || lim->max_k > DS_SEL_MAX_K) return DS_SEL_E_INVALID;
   if (lim->max_blocks < 0 || lim->max_blocks > DS_SEL_MAX_BLOCKS) return DS_SEL_E_INVALID;
-  if ((lim->flags & ~DS_SEL_FLAG_VALU_SCORE) != 0 || lim->device < 0) return DS_SEL_E_INVALID;
+  if ((lim->flags & ~kKnownFlags) != 0 || lim->device < 0) return DS_SEL_E_INVALID;
   return DS_SEL_OK;
 }
 
@@ -96,6 +98,12 @@ int check_args(const ds_sel_limits& lim, const ds_sel_args* a, const ds_sel_q8_k
   if (a->layers > lim.max_layers || a->rows > lim.max_rows || a->heads > lim.max_heads ||
       a->dim > lim.max_dim || a->k > lim.max_k || a->blocks > lim.max_blocks)
     return DS_SEL_E_CAPACITY;
+  if (lim.flags & DS_SEL_FLAG_HEAD_RELU) {
+    // the per-head ReLU score: bf16 keys on the matrix cores, heads staged in LDS
+    if (k8 || (lim.flags & DS_SEL_FLAG_VALU_SCORE)) return DS_SEL_E_UNSUPPORTED;
+    if (dssel::relu_stage_bytes(a->rows, a->heads, a->dim) + 16 > dssel::kReluStageBytes)
+      return DS_SEL_E_UNSUPPORTED;
+  }
   if (!a->q || !a->w || !a->out_idx || !a->out_score) return DS_SEL_E_INVALID;
   if (!aligned(a->q, 16) || !aligned(a->w, 2) || !aligned(a->out_idx, 4) ||
       !aligned(a->out_score, 4) || !aligned(a->out_count, 4) || !aligned(a->limit, 4) ||
@@ -443,7 +451,7 @@ int64_t ds_sel_noalloc_scratch_bytes(const ds_sel_args* a) {
 
 int ds_sel_score_select_noalloc(int32_t device, uint32_t flags, const ds_sel_args* a,
                                 void* hip_stream) {
-  if (device < 0 || device >= kMaxDevices || (flags & ~DS_SEL_FLAG_VALU_SCORE) != 0)
+  if (device < 0 || device >= kMaxDevices || (flags & ~(uint32_t)kKnownFlags) != 0)
     return DS_SEL_E_INVALID;
   // Checks against the build's hard limits only; the static array decides the rest.
   ds_sel_limits lim{};
@@ -602,6 +610,7 @@ int enqueue(const Target& t, const ds_sel_args* a, void* hip_stream, void* const
                     : ((a->mask_row_stride == 0 || a->rows == 1) ? dssel::kSharedMask
                                                                  : dssel::kRowMask);
   c.engine = (t.flags & DS_SEL_FLAG_VALU_SCORE) ? dssel::kEngineValu : dssel::kEngineMfma;
+  c.score_kind = (t.flags & DS_SEL_FLAG_HEAD_RELU) ? dssel::kScoreHeadRelu : dssel::kScoreLinear;
   c.fmt = k8 ? dssel::kKeysQ8 : dssel::kKeysBf16;
   if (k8) {
     c.codes = k8->codes;

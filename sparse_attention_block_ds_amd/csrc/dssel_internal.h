@@ -56,9 +56,25 @@ enum Engine : int {
 };
 
 // Everything one call needs, in element units, passed by value to kernels.
+// The block score: the linear sum_h w_h (q_h . K) (folded), or the per-head
+// ReLU variant sum_h w_h max(q_h . K, 0) (unfolded: every head on the matrix cores).
+enum ScoreKind : int {
+  kScoreLinear = 0,
+  kScoreHeadRelu = 1,
+};
+
+// The per-head ReLU kernels stage a layer's query heads and weights in LDS:
+// bf16 q [R][Hp][d + 8] (rows padded by 16 bytes) then fp32 w [R][Hp], with
+// Hp = H rounded up to 16 and zeros past H.  The stage must fit this budget.
+constexpr int kReluStageBytes = 120 * 1024;
+constexpr int64_t relu_stage_bytes(int64_t rows, int64_t heads, int64_t dim) {
+  return rows * ((heads + 15) / 16 * 16) * (2 * (dim + 8) + 4);
+}
+
 struct Call {
   int32_t layers, rows, heads, dim, k;
   int32_t mode, engine;
+  int32_t score_kind;   // ScoreKind
   int32_t ntiles;     // ceil(N / kTileBlocks)
   int32_t score_wgs;    // score grid: >= layers + ceil(L * N / kScorePieceMax)
   int32_t score_slots;  // resident score workgroups on the device

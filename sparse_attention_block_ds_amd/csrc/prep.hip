@@ -39,6 +39,7 @@
 // rank taken is 19, so a rescore is a ~1e-8 event.
 #include "device_util.h"
 #include "dssel_internal.h"
+#include "relu_heads.h"
 
 namespace dssel {
 namespace {
@@ -105,7 +106,10 @@ __device__ __forceinline__ uint32_t row_word(const Call& c, const uint32_t* mask
 
 // LDS of the fold workgroup and of the expanding workgroups (never both).
 struct FoldShared {
-  float part[kPrepThreads * 8];            // fold partial sums, [head slice][r * d + i]
+  union {
+    float part[kPrepThreads * 8];          // fold partial sums, [head slice][r * d + i]
+    uint32_t relu[kReluStageBytes / 4];    // per-head ReLU score: the layer's q heads and w
+  };
   float q[kMaxRows][256];                  // folded query rows
   uint32_t skey[kMaxRows][kSampleSlots];   // sample keys (0: not admitted by the row)
   int64_t lim[kMaxRows];                   // the rows' limits, clamped to [0, N]
@@ -146,6 +150,7 @@ constexpr int kGroupsPerWave = kSampleGroups / (kPrepThreads / kWave);  // 2
 // block l % 16.  Each wave takes groups wave and wave + 16 of 16 slots.
 template <int R, int D>
 struct SampleMfma {
+  static constexpr bool kFold = true;  // scores on the folded query
   static constexpr int KC = D / 32;
   u32x4_t kb[kGroupsPerWave][KC];
   uint32_t mw[kGroupsPerWave][4];  // mask words of rows 4 (lane / 16) + i at the lane's block
@@ -179,6 +184,8 @@ struct SampleMfma {
       }
     }
   }
+
+  __device__ void stage(const Call&, int, FoldShared&) {}
 
   __device__ void finish(int64_t n, int S, FoldShared& sh) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -221,6 +228,7 @@ struct SampleMfma {
 // block's group scale and summed in fp32.
 template <int R, int D>
 struct SampleMfmaQ8 {
+  static constexpr bool kFold = true;
   static constexpr int KC = D / 32;
   uint2 kb[kGroupsPerWave][KC];
   uint16_t ks[kGroupsPerWave][KC];
@@ -263,6 +271,8 @@ struct SampleMfmaQ8 {
     }
   }
 
+  __device__ void stage(const Call&, int, FoldShared&) {}
+
   __device__ void finish(int64_t n, int S, FoldShared& sh) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int m = lane & 15;
@@ -298,6 +308,71 @@ struct SampleMfmaQ8 {
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * (lane >> 4) + i;
           if (r < R && b < sh.lim[r] && ((mw[g][i] >> (b & 31)) & 1u)) sh.skey[r][j] = score_to_key(sc[i]);
+        }
+      }
+    }
+  }
+};
+
+// Sampled keys under the per-head ReLU score: the same sampled blocks and
+// mask words as SampleMfma, scored against every (row, head) pair on the
+// matrix cores (relu_heads.h) with the layer's heads staged in LDS; no fold.
+template <int R, int D>
+struct SampleRelu {
+  static constexpr bool kFold = false;
+  static constexpr int KC = D / 32;
+  relu_u32x4_t kb[kGroupsPerWave][KC];
+  uint32_t mw[kGroupsPerWave][4];
+  ReluStage st;
+
+  __device__ void issue(const Call& c, int l, int64_t n, const uint32_t* mask_l, int S) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const uint16_t* K = c.keys + (int64_t)l * c.key_layer_stride;
+#pragma unroll
+    for (int g = 0; g < kGroupsPerWave; ++g) {
+      const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) kb[g][cc] = relu_u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mw[g][i] = 0xFFFFFFFFu;
+      if (j < S) {
+        const int64_t b = sample_block(j, n);
+        const uint16_t* row = K + b * c.ldk + 8 * (lane >> 4);
+#pragma unroll
+        for (int cc = 0; cc < KC; ++cc) kb[g][cc] = *reinterpret_cast<const relu_u32x4_t*>(row + 32 * cc);
+        if (c.mode == kSharedMask) {
+          const uint32_t w = mask_l[b >> 5];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mw[g][i] = w;
+        } else if (c.mode == kRowMask) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * (lane >> 4) + i;
+            if (r < R) mw[g][i] = mask_l[r * c.mask_row_stride + (b >> 5)];
+          }
+        }
+      }
+    }
+  }
+
+  __device__ void stage(const Call& c, int l, FoldShared& sh) {
+    st = relu_stage_heads<R, D>(c, l, sh.relu, threadIdx.x, kPrepThreads);
+  }
+
+  // Row r's score of a sampled block is complete in all four lanes of its
+  // column; the lanes of group r / 4 hold row r's mask word and store it.
+  __device__ void finish(int64_t n, int S, FoldShared& sh) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float sc[kGroupsPerWave];
+      relu_row_scores<D, kGroupsPerWave>(st, r, kb, sc);
+#pragma unroll
+      for (int g = 0; g < kGroupsPerWave; ++g) {
+        const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
+        if ((lane >> 4) == r / 4 && j < S) {
+          const int64_t b = sample_block(j, n);
+          if (b < sh.lim[r] && ((mw[g][r % 4] >> (b & 31)) & 1u)) sh.skey[r][j] = score_to_key(sc[g]);
         }
       }
     }
@@ -353,11 +428,13 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
   for (int i = tid; i < kMaxRows * kSampleSlots; i += kPrepThreads) (&sh.skey[0][0])[i] = 0u;
 
   // fold, first half: thread (slice hs, chunk) sums w_h q_h[i0 .. i0 + 8) over
-  // its slice of heads, ascending h, eight heads' loads at a time
+  // its slice of heads, ascending h, eight heads' loads at a time.  The
+  // per-head ReLU score has no fold: its sampler stages the heads instead.
   const int chunks = R * D / 8;
   const int slices = kPrepThreads / chunks;  // >= 4
   const int hper = (H + slices - 1) / slices;
-  if (tid < chunks * slices) {
+  if constexpr (!Sampler::kFold) smp.stage(c, l, sh);
+  if (Sampler::kFold && tid < chunks * slices) {
     const int ch = tid % chunks, hs = tid / chunks;
     const int r = ch / (D / 8), i0 = (ch % (D / 8)) * 8;
     const int64_t lr = (int64_t)l * R + r;
@@ -434,7 +511,7 @@ __device__ void fold_count_floor(const Call& c, int l, FoldShared& sh) {
 
   // fold, second half: the slices' partial sums in ascending slice order; the
   // three-way bf16 split (exact for |q~_i| >= 2^-110)
-  for (int o = tid; o < R * D; o += kPrepThreads) {
+  for (int o = tid; Sampler::kFold && o < R * D; o += kPrepThreads) {
     const int r = o / D, i = o % D;
     const int64_t lr = (int64_t)l * R + r;
     float acc = 0.0f;
@@ -541,6 +618,8 @@ template <int R, int D>
 void launch_rd(const Call& c, dim3 grid, hipStream_t stream) {
   if (c.fmt == kKeysQ8)
     hipLaunchKernelGGL((prep_kernel<R, D, SampleMfmaQ8<R, D>>), grid, dim3(kPrepThreads), 0, stream, c);
+  else if (c.score_kind == kScoreHeadRelu)
+    hipLaunchKernelGGL((prep_kernel<R, D, SampleRelu<R, D>>), grid, dim3(kPrepThreads), 0, stream, c);
   else
     hipLaunchKernelGGL((prep_kernel<R, D, SampleMfma<R, D>>), grid, dim3(kPrepThreads), 0, stream, c);
 }

@@ -40,6 +40,7 @@
 //     their size.
 #include "device_util.h"
 #include "dssel_internal.h"
+#include "relu_heads.h"
 
 namespace dssel {
 namespace {
@@ -194,7 +195,7 @@ struct MfmaEngine {
   bf16x8_t a[S][KC];                      // A operand: q~ parts (row m = lane % 16)
   u32x4_t buf[NBUF][KC];                  // B operand: K rows (block = lane % 16)
 
-  __device__ void init(const Call& c, int l) {
+  __device__ void init(const Call& c, int l, uint32_t*) {
     const int lane = lane_id();
     const int m = lane & 15, g = lane >> 4;
     const int p = m & 3;
@@ -285,7 +286,7 @@ struct MfmaQ8Engine {
   const uint16_t* scales_l;
   int64_t ldc, lds;
 
-  __device__ void init(const Call& c, int l) {
+  __device__ void init(const Call& c, int l, uint32_t*) {
     const int lane = lane_id();
     const int m = lane & 15, g = lane >> 4;
     const int p = m & 3;
@@ -370,6 +371,77 @@ struct MfmaQ8Engine {
   }
 };
 
+// ------------------------------------------------------ per-head ReLU engine
+// The unfolded score sum_h w_h max(q_h . K, 0): the key rows load as for the
+// MFMA engine (block = lane % 16, 16 bytes per 32 columns); each row's score
+// is R x (H / 16) x (d / 32) MFMAs against the heads staged in LDS
+// (relu_heads.h), complete in all four lanes of a block.  The lanes of group
+// g then offer row 4 s + g of set s, as the MFMA engine's do.
+template <int R, int D, int NBUF>
+struct ReluEngine {
+  static constexpr int kRows = R, kBuffers = NBUF;
+  static constexpr int KC = D / 32;
+  static constexpr int S = (R + 3) / 4;
+  relu_u32x4_t buf[NBUF][1][KC];
+  ReluStage st;
+
+  __device__ void init(const Call& c, int l, uint32_t* lds) {
+    st = relu_stage_heads<R, D>(c, l, lds, threadIdx.x, kScoreThreads);
+  }
+
+  template <int B>
+  __device__ __forceinline__ void load(const PieceCtx<R>& t, const uint16_t* K, int64_t ldk, int g0) {
+    const int lane = lane_id();
+    const int e = g0 + (lane & 15);
+    if (t.valid(e)) {
+      const uint16_t* row = K + (int64_t)t.block_of(e) * ldk + 8 * (lane >> 4);
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) buf[B][0][cc] = load16(row + 32 * cc);
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc) buf[B][0][cc] = relu_u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  template <int B>
+  __device__ __forceinline__ void compute_emit(PieceCtx<R>& t, int g0) {
+    float sc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float o[1];
+      relu_row_scores<D, 1>(st, r, buf[B], o);
+      sc[r] = o[0];
+    }
+    const int lane = lane_id();
+    const int e = g0 + (lane & 15), g = lane >> 4;
+    const int pos = t.pos_of(e);
+    const bool live = e < t.cnt;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      float v = sc[0];
+#pragma unroll
+      for (int r = 1; r < R; ++r)
+        if (r == 4 * s + g) v = sc[r];
+      const uint32_t key = score_to_key(v);
+      bool ok = live && pos < lp[s] && key >= lf[s];
+      if (t.mode == kRowMask && ok) ok = t.row_admits(4 * s + g, e);
+      t.append(ok, key, pos, 4 * s + g);
+    }
+  }
+
+  int lp[S];
+  uint32_t lf[S];
+  __device__ void bind_rows(const ScoreShared<R>& sh) {
+    const int g = lane_id() >> 4;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int r = 4 * s + g;
+      lp[s] = r < R ? sh.P[r] : 0;
+      lf[s] = r < R ? sh.floor[r] : 0u;
+    }
+  }
+};
+
 // ---------------------------------------------------------------- VALU engine
 template <int R, int D, int NBUF>
 struct ValuEngine {
@@ -380,7 +452,7 @@ struct ValuEngine {
   float qv[R][8];
   u32x4_t buf[NBUF][U];
 
-  __device__ void init(const Call& c, int l) {
+  __device__ void init(const Call& c, int l, uint32_t*) {
     const int slice = lane_id() % LPR;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -532,7 +604,7 @@ __device__ __forceinline__ Piece find_piece(const Call& c, int* shared_out) {
 }
 
 template <int R, int D, class Engine>
-__device__ __forceinline__ void score_body(const Call& c) {
+__device__ __forceinline__ void score_body(const Call& c, uint32_t* relu_lds) {
   __shared__ ScoreShared<R> sh;
   const int tid = threadIdx.x, wave = tid / kWave;
   const int64_t N = c.blocks;
@@ -579,7 +651,7 @@ __device__ __forceinline__ void score_body(const Call& c) {
     sh.lim[tid] = v < 0 ? 0 : (v > N ? N : v);
   }
   Engine eng;
-  eng.init(c, sl);
+  eng.init(c, sl, relu_lds);
   __syncthreads();
 
   pc.mode = c.mode;
@@ -622,12 +694,20 @@ __device__ __forceinline__ void score_body(const Call& c) {
 template <int R, int D, class Engine, int W>
 __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(W, 8)))
 void score_kernel_mfma(Call c) {
-  score_body<R, D, Engine>(c);
+  score_body<R, D, Engine>(c, nullptr);
 }
 
 template <int R, int D, class Engine>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel_valu(Call c) {
-  score_body<R, D, Engine>(c);
+  score_body<R, D, Engine>(c, nullptr);
+}
+
+// The per-head ReLU kernel: one workgroup per compute unit holds the layer's
+// heads (up to 120 KiB of LDS), so its four waves each run one SIMD.
+template <int R, int D>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel_relu(Call c) {
+  __shared__ uint32_t relu_lds[kReluStageBytes / 4];
+  score_body<R, D, ReluEngine<R, D, 3>>(c, relu_lds);
 }
 
 // Load buffers per wave: two groups of key rows in flight; one at d = 256,
@@ -641,6 +721,8 @@ hipError_t launch_rd(const Call& c, dim3 grid, hipStream_t s) {
   if (c.fmt == kKeysQ8)
     hipLaunchKernelGGL((score_kernel_mfma<R, D, MfmaQ8Engine<R, D, kRing<D>>, kMfmaWaves>), grid,
                        dim3(kScoreThreads), 0, s, c);
+  else if (c.score_kind == kScoreHeadRelu)
+    hipLaunchKernelGGL((score_kernel_relu<R, D>), grid, dim3(kScoreThreads), 0, s, c);
   else if (c.engine == kEngineValu)
     hipLaunchKernelGGL((score_kernel_valu<R, D, ValuEngine<R, D, kRing<D>>>), grid,
                        dim3(kScoreThreads), 0, s, c);

@@ -265,7 +265,30 @@ static __device__ int rescore_row(const Call& c, int l, int r, uint64_t* words, 
       if (mrow) adm = ((mrow[b >> 5] >> (b & 31)) & 1u) && (int64_t)b < lim;
     }
     uint64_t w = 0;
-    if (adm && c.fmt == kKeysQ8) {
+    if (adm && c.score_kind == kScoreHeadRelu) {
+      // per-head ReLU: every head's dot product against the bf16 key row,
+      // clamped at zero and weighted, heads in ascending order
+      const int H = c.heads;
+      const uint16_t* krow = K + (int64_t)b * c.ldk;
+      const uint16_t* qrow = c.q + lr * H * D;
+      const uint16_t* wrow = c.w + lr * H;
+      float s = 0.0f;
+      for (int h = 0; h < H; ++h) {
+        float dot = 0.0f;
+        for (int i = 0; i < D; i += 8) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(krow + i);
+          const uint4 qv = *reinterpret_cast<const uint4*>(qrow + (int64_t)h * D + i);
+          const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w}, q4[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dot = fmaf(bf16_lo(q4[e]), bf16_lo(k4[e]), dot);
+            dot = fmaf(bf16_hi(q4[e]), bf16_hi(k4[e]), dot);
+          }
+        }
+        s += bf16_to_f32(wrow[h]) * fmaxf(dot, 0.0f);
+      }
+      w = pack(score_to_key(s), p);
+    } else if (adm && c.fmt == kKeysQ8) {
       // 8-bit keys: per 32-column group, sum q~_i c_i, then add scale times that
       const int8_t* crow = c.codes + (int64_t)l * c.code_layer_stride + (int64_t)b * c.ldc;
       const uint16_t* srow = c.scales + (int64_t)l * c.scale_layer_stride + (int64_t)b * c.lds;

@@ -23,6 +23,7 @@ DS_SEL_E_HIP = 4
 DS_SEL_E_NOMEM = 5
 DS_SEL_E_UNSUPPORTED = 6
 DS_SEL_FLAG_VALU_SCORE = 1
+DS_SEL_FLAG_HEAD_RELU = 2
 
 EXPORTED = ("ds_sel_create", "ds_sel_score_select", "ds_sel_score_select_profiled",
             "ds_sel_destroy", "ds_sel_check_args", "ds_sel_scratch_bytes", "ds_sel_status_string",
@@ -160,6 +161,16 @@ def status_string(status: int) -> str:
         return load_library().ds_sel_status_string(status).decode()
     except RuntimeError:
         return "status"
+
+
+def selector_flags(engine="mfma", score="linear"):
+    """DS_SEL_FLAG_* bits for a key-stream engine and a score formula."""
+    if engine not in ("mfma", "valu"):
+        raise ValueError("engine must be 'mfma' or 'valu'")
+    if score not in ("linear", "relu"):
+        raise ValueError("score must be 'linear' or 'relu'")
+    return ((DS_SEL_FLAG_VALU_SCORE if engine == "valu" else 0) |
+            (DS_SEL_FLAG_HEAD_RELU if score == "relu" else 0))
 
 
 def make_limits(max_layers, max_rows, max_heads, max_dim, max_blocks, max_k=512, device=0,
@@ -353,15 +364,15 @@ class Selector:
     """One libdssel handle: scratch sized for the given capacity on one device."""
 
     def __init__(self, max_layers, max_rows, max_heads, max_dim, max_blocks, max_k=512,
-                 device: Optional[int] = None, engine: str = "mfma"):
+                 device: Optional[int] = None, engine: str = "mfma", score: str = "linear"):
+        """engine "mfma" (default) or "valu" for the key stream; score "linear"
+        (sum_h w_h q_h . K) or "relu" (sum_h w_h max(q_h . K, 0))."""
         import torch
         self._torch = torch
         self.lib = load_library()
         self.device = torch.cuda.current_device() if device is None else device
-        if engine not in ("mfma", "valu"):
-            raise ValueError("engine must be 'mfma' or 'valu'")
         self.limits = make_limits(max_layers, max_rows, max_heads, max_dim, max_blocks, max_k,
-                                  self.device, DS_SEL_FLAG_VALU_SCORE if engine == "valu" else 0)
+                                  self.device, selector_flags(engine, score))
         h = ctypes.c_void_p()
         rc = self.lib.ds_sel_create(ctypes.byref(self.limits), ctypes.byref(h))
         if rc != DS_SEL_OK:
@@ -522,13 +533,13 @@ def calibrate(kind, workgroups, sink, keys=None, mask=None, ranges=None, stream=
         raise DsSelError(rc, "ds_sel_calibrate")
 
 
-def score_select_noalloc(q, w, keys, k, mask, limit, out, device=None, engine="mfma", stream=None):
+def score_select_noalloc(q, w, keys, k, mask, limit, out, device=None, engine="mfma", stream=None,
+                         score="linear"):
     """ds_sel_score_select_noalloc: the selection on the library's static
     scratch, with caller-provided outputs (idx, score, count) and no handle.
     Calls overlapping in time on one GPU race (they share the scratch)."""
     import torch
-    if engine not in ("mfma", "valu"):
-        raise ValueError("engine must be 'mfma' or 'valu'")
+    flags = selector_flags(engine, score)
     if out is None:
         raise ValueError("out (idx, score, count) is required: this entry point allocates nothing")
     dev = q.device if device is None else torch.device("cuda", device)
@@ -538,8 +549,7 @@ def score_select_noalloc(q, w, keys, k, mask, limit, out, device=None, engine="m
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
-    rc = lib.ds_sel_score_select_noalloc(dev.index, DS_SEL_FLAG_VALU_SCORE if engine == "valu" else 0,
-                                         ctypes.byref(a), ctypes.c_void_p(handle))
+    rc = lib.ds_sel_score_select_noalloc(dev.index, flags, ctypes.byref(a), ctypes.c_void_p(handle))
     if rc != DS_SEL_OK:
         raise DsSelError(rc, "ds_sel_score_select_noalloc")
     return out

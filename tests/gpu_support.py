@@ -30,8 +30,8 @@ def run_gpu(selector: sel.Selector, p: wl.Problem, k=None):
     return idx.cpu().numpy(), score.cpu().numpy(), count.cpu().numpy()
 
 
-def run_oracle(p: wl.Problem, k=None):
-    return oracle.select(p.q, p.w, p.keys, p.k if k is None else k, p.mask, p.limit)
+def run_oracle(p: wl.Problem, k=None, score="linear"):
+    return oracle.select(p.q, p.w, p.keys, p.k if k is None else k, p.mask, p.limit, score=score)
 
 
 def sub_problem(p: wl.Problem, l, r):
@@ -42,7 +42,7 @@ def sub_problem(p: wl.Problem, l, r):
                       None if p.limit is None else p.limit[l:l + 1, r:r + 1], p.integer_valued)
 
 
-def oracle_pairs(p: wl.Problem, pairs, threads=8):
+def oracle_pairs(p: wl.Problem, pairs, threads=8, score="linear"):
     """The oracle's result for each (layer, row) of `pairs`, on a pool of host
     threads (ctypes releases the GIL while the oracle runs)."""
     from concurrent.futures import ThreadPoolExecutor
@@ -50,7 +50,7 @@ def oracle_pairs(p: wl.Problem, pairs, threads=8):
 
     def one(lr):
         sub = sub_problem(p, *lr)
-        return oracle.select(sub.q, sub.w, sub.keys, sub.k, sub.mask, sub.limit, lib=lib)
+        return oracle.select(sub.q, sub.w, sub.keys, sub.k, sub.mask, sub.limit, lib=lib, score=score)
     with ThreadPoolExecutor(threads) as ex:
         return list(ex.map(one, pairs))
 

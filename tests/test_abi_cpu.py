@@ -185,7 +185,7 @@ def test_capacity_enforced(lib, field, value):
 
 
 def test_bad_limits_rejected(lib):
-    for field, value in [("max_rows", 9), ("max_k", 4097), ("max_layers", 0), ("max_dim", 512), ("flags", 2),
+    for field, value in [("max_rows", 9), ("max_k", 4097), ("max_layers", 0), ("max_dim", 512), ("flags", 4),
                          ("max_blocks", -1)]:
         lim = sel.make_limits(**LIM)
         setattr(lim, field, value)
@@ -392,3 +392,22 @@ def test_quantize_checks_before_touching_a_device(lib):
     if os.path.exists("/dev/kfd"):
         pytest.skip("a GPU driver is present on this host")
     assert lib.ds_sel_quantize_q8(ctypes.byref(_quant_args()), None) == sel.DS_SEL_E_NODEVICE
+
+
+# ------------------------------------------------------------ the per-head ReLU score
+def test_head_relu_supported_where_the_heads_fit(lib):
+    relu = sel.DS_SEL_FLAG_HEAD_RELU
+    lim8 = dict(max_rows=8)
+    assert check(lib, _args(R=6), flags=relu) == sel.DS_SEL_OK          # 6 x 64 heads x d 128
+    assert check(lib, _args(R=1, H=64, d=128), flags=relu) == sel.DS_SEL_OK
+    # 8 rows x 64 heads x (2 (128 + 8) + 4) bytes = 141,312 > the stage
+    assert check(lib, _args(R=8), flags=relu, **lim8) == sel.DS_SEL_E_UNSUPPORTED
+    assert check(lib, _args(R=8, H=48), flags=relu, **lim8) == sel.DS_SEL_OK
+    # with the vector-ALU engine, or on the 8-bit stream: not built
+    assert check(lib, _args(R=6), flags=relu | sel.DS_SEL_FLAG_VALU_SCORE) == sel.DS_SEL_E_UNSUPPORTED
+    limits = sel.make_limits(**{**LIM, "flags": relu})
+    assert lib.ds_sel_check_args_q8(ctypes.byref(limits), ctypes.byref(_q8_args()),
+                                    ctypes.byref(_q8())) == sel.DS_SEL_E_UNSUPPORTED
+    assert sel.selector_flags("mfma", "relu") == relu
+    with pytest.raises(ValueError):
+        sel.selector_flags("mfma", "tanh")
