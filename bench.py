@@ -32,7 +32,9 @@ Prints one JSON line on stdout.  Besides the contract's keys it carries:
   attend         attention over the last step's selection (not part of value);
   q8             the same workload with the keys as the 8-bit stream (int8
                  codes, one fp16 scale per 32): throughput and its own
-                 roofline on that stream's algorithmic bytes (not part of value).
+                 roofline on that stream's algorithmic bytes (not part of value);
+  relu           the same workload under the per-head ReLU score: the score
+                 kernel's flops against the bf16 MFMA peak (not part of value).
 """
 from __future__ import annotations
 
@@ -48,6 +50,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 MALL_BYTES = 256 << 20
 COLD_BYTES = 2 * MALL_BYTES
 PROFILES = os.path.join(ROOT, "profiles")
@@ -83,6 +86,7 @@ def parse():
     ap.add_argument("--no-singles", action="store_true", help="skip the single-call legs")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the calibration launches")
     ap.add_argument("--no-q8", action="store_true", help="skip the 8-bit key stream leg")
+    ap.add_argument("--no-relu", action="store_true", help="skip the per-head ReLU score leg")
     ap.add_argument("--calls", type=int, default=200,
                     help="event-bracketed calls per single-call leg")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -185,7 +189,7 @@ def pct(xs):
 class Runner:
     """One workload on the device: rotated input copies, outputs, a handle."""
 
-    def __init__(self, p, engine, stream, sets=None, fmt="bf16"):
+    def __init__(self, p, engine, stream, sets=None, fmt="bf16", score="linear"):
         import numpy as np
         import torch
         from sparse_attention_block_ds_amd import selector as sel
@@ -207,7 +211,7 @@ class Runner:
         self.n_sets = n
         self.selector = sel.Selector(max_layers=p.layers, max_rows=p.rows, max_heads=p.heads,
                                      max_dim=p.dim, max_blocks=p.blocks, max_k=p.k, device=0,
-                                     engine=engine)
+                                     engine=engine, score=score)
         L, R, k = p.layers, p.rows, p.k
         self.outs = [(torch.empty((L, R, k), dtype=torch.int32, device="cuda:0"),
                       torch.empty((L, R, k), dtype=torch.float32, device="cuda:0"),
@@ -506,6 +510,55 @@ def q8_leg(p, stream, steps, warmup):
     }
 
 
+def relu_leg(p, stream, steps, warmup):
+    """The same workload under the per-head ReLU score (a handle created with
+    DS_SEL_FLAG_HEAD_RELU): every (row, head) pair meets every admitted key, so
+    the score kernel is a matrix-core contraction.  Its algorithmic work is
+    2 H d flops per admitted (row, block) pair; it is reported against the
+    dense bf16 MFMA peak, with the key bytes against the HBM peak beside it.
+    Sampled (layer, row) selections are checked against the oracle's ReLU
+    selection (bit-exact on integer inputs, else the tolerance + set rule)."""
+    import oracle
+    t0 = time.perf_counter()
+    run = Runner(p, "mfma", stream, score="relu")
+    log(f"[bench] relu leg: {run.n_sets} input copies, ready in {time.perf_counter() - t0:.1f}s")
+    wall_ms, dev_ms = time_back_to_back(run, steps, warmup)
+    call_us, kernels = per_call(run, steps)
+    out = run.output(steps - 1)
+    lib = oracle.load()
+    pairs = [(l, r) for l in sorted({0, p.layers // 2, p.layers - 1}) for r in sorted({0, p.rows - 1})]
+    bad = 0
+    for l, r in pairs:
+        sub = _sub_problem(p, l, r)
+        ora = oracle.select(sub.q, sub.w, sub.keys, sub.k, sub.mask, sub.limit, lib=lib, score="relu")
+        scorer = lambda blocks: oracle.score_blocks(sub.q, sub.w, sub.keys, 0, 0, blocks, lib=lib,
+                                                    score="relu")
+        if p.integer_valued:
+            scorer = None
+        bad += 0 if _accept(p, sub, out, l, r, ora, lib, scorer=scorer) else 1
+    candidates, alg, n_sets = run.candidates, run.alg, run.n_sets
+    run.close()
+    if bad:
+        log(f"[bench] PARITY FAILURE in the relu leg: {bad} of {len(pairs)} pairs")
+        sys.exit(3)
+    flops = 2.0 * p.heads * p.dim * candidates
+    tflops = flops / (kernels["score"] * 1e-6) / 1e12
+    score_gbs = alg["keys"] / (kernels["score"] * 1e-6) / 1e9
+    return {
+        "workload": WORKLOADS[p.name] + ", score sum_h w_h max(q_h . K, 0)",
+        "input_copies": n_sets, "ms_per_step": wall_ms, "device_ms_per_step": dev_ms,
+        "candidate_blocks_per_s": candidates / (wall_ms * 1e-3),
+        "device_us_per_call": call_us, "kernels_us_median": kernels,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "kernel": "score (per-head ReLU, bf16 MFMA)",
+                     "flops_per_step": flops, "flops_per_candidate": 2 * p.heads * p.dim,
+                     "key_bytes_gbs": score_gbs, "key_bytes_frac_hbm": score_gbs / HBM_PEAK_GBS},
+        "parity": f"{len(pairs)} (layer,row) pairs vs the oracle's ReLU selection "
+                  + ("bit-exact" if p.integer_valued else "(tolerance + set rule)"),
+    }
+
+
 def attend_leg(run, steps):
     """Attention over the last step's selection (64 query heads per row, bf16 q
     and values drawn on the device from a fixed seed), timed with HIP events on
@@ -630,6 +683,19 @@ def main():
             log(f"[bench] {name}: {json.dumps(singles[name]['device_us_per_call'])} us per call")
             torch.cuda.empty_cache()
 
+    relu = None
+    if not args.no_relu:
+        from sparse_attention_block_ds_amd import selector as sel_mod
+        try:
+            relu = relu_leg(p, stream, args.steps, args.warmup)
+            log(f"[bench] relu leg: {relu['ms_per_step']:.4f} ms per step, score kernel "
+                f"{relu['roofline']['frac']:.3f} of the bf16 MFMA peak")
+        except sel_mod.DsSelError as e:  # heads too many for the LDS stage at this shape
+            if e.status != sel_mod.DS_SEL_E_UNSUPPORTED:
+                raise
+            relu = {"skipped": str(e)}
+        torch.cuda.empty_cache()
+
     q8 = None
     if not args.no_q8 and p.dim % 32 == 0:
         q8 = q8_leg(p, stream, args.steps, args.warmup)
@@ -676,6 +742,7 @@ def main():
         "single_calls": singles,
         "attend": attend,
         "q8": q8,
+        "relu": relu,
     }
     print(json.dumps(line), flush=True)
 

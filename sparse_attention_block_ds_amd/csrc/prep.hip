@@ -363,10 +363,17 @@ struct SampleRelu {
   // column; the lanes of group r / 4 hold row r's mask word and store it.
   __device__ void finish(int64_t n, int S, FoldShared& sh) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
+    float all[R][kGroupsPerWave];
+#pragma unroll
+    for (int g = 0; g < kGroupsPerWave; ++g) {  // one group at a time: 128 registers
+      float one[R][1];
+      relu_all_rows<R, D, 1, false>(st, reinterpret_cast<const relu_u32x4_t(&)[1][KC]>(kb[g]), one);
+#pragma unroll
+      for (int r = 0; r < R; ++r) all[r][g] = one[r][0];
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float sc[kGroupsPerWave];
-      relu_row_scores<D, kGroupsPerWave>(st, r, kb, sc);
+      const float (&sc)[kGroupsPerWave] = all[r];
 #pragma unroll
       for (int g = 0; g < kGroupsPerWave; ++g) {
         const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);

@@ -107,4 +107,97 @@ __device__ __forceinline__ void relu_row_scores(const ReluStage& st, int r,
   }
 }
 
+// Every row's score of NG groups of 16 blocks at once: head tiles outside,
+// rows inside, so that each tile issues R x NG independent MFMA chains.  The
+// A fragments (R x d/32 LDS reads) of tile t + 16 are read while tile t's
+// MFMAs run, and tile t's clamp and weighting run after both are issued, so
+// neither the LDS latency nor the MFMA latency is waited out per instruction.
+template <int R, int D>
+__device__ __forceinline__ void relu_read_tile(const uint16_t* qbase, int hp, int t,
+                                               relu_u32x4_t (&a)[R][D / 32]) {
+  constexpr int KC = D / 32, QS = D + 8;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int cc = 0; cc < KC; ++cc)
+      a[r][cc] = *reinterpret_cast<const relu_u32x4_t*>(qbase + ((int64_t)r * hp + t) * QS + 32 * cc);
+}
+
+__device__ __forceinline__ float relu_clamp(float x) {
+  return __builtin_amdgcn_fmed3f(x, 0.0f, __builtin_huge_valf());  // max(x, 0) for finite x
+}
+
+// PIPE = false: the fragments are read inside the tile (no prefetch registers),
+// for kernels held to 128 registers whose other waves hide the latency.
+template <int R, int D, int NG, bool PIPE = true>
+__device__ __forceinline__ void relu_all_rows(const ReluStage& st, const relu_u32x4_t (&kb)[NG][D / 32],
+                                              float (&out)[R][NG]) {
+  constexpr int KC = D / 32, QS = D + 8;
+  const int lane = lane_id();
+  const int m = lane & 15, g = lane >> 4;
+  float part[R][NG];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int n = 0; n < NG; ++n) part[r][n] = 0.0f;
+  const uint16_t* qbase = st.q + (int64_t)m * QS + 8 * g;
+  const float* wbase = st.w + 4 * g;
+  relu_u32x4_t a[PIPE ? R : 1][KC];
+  if constexpr (PIPE) relu_read_tile<R, D>(qbase, st.hp, 0, a);
+  for (int t = 0; t < st.hp; t += 16) {
+    relu_f32x4_t acc[R][NG];
+    if constexpr (!PIPE) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int cc = 0; cc < KC; ++cc) {
+          const relu_u32x4_t x =
+              *reinterpret_cast<const relu_u32x4_t*>(qbase + ((int64_t)r * st.hp + t) * QS + 32 * cc);
+#pragma unroll
+          for (int n = 0; n < NG; ++n)
+            acc[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(relu_bf16x8_t, x), __builtin_bit_cast(relu_bf16x8_t, kb[n][cc]),
+                cc == 0 ? relu_f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[r][n], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < KC; ++cc)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int n = 0; n < NG; ++n)
+            acc[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(relu_bf16x8_t, a[PIPE ? r : 0][cc]),
+                __builtin_bit_cast(relu_bf16x8_t, kb[n][cc]),
+                cc == 0 ? relu_f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[r][n], 0, 0, 0);
+    }
+    float4 w4[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) w4[r] = *reinterpret_cast<const float4*>(wbase + r * st.hp + t);
+    if constexpr (PIPE) {
+      if (t + 16 < st.hp) relu_read_tile<R, D>(qbase, st.hp, t + 16, a);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int n = 0; n < NG; ++n) {
+        part[r][n] += w4[r].x * relu_clamp(acc[r][n][0]);
+        part[r][n] += w4[r].y * relu_clamp(acc[r][n][1]);
+        part[r][n] += w4[r].z * relu_clamp(acc[r][n][2]);
+        part[r][n] += w4[r].w * relu_clamp(acc[r][n][3]);
+      }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int n = 0; n < NG; ++n) {
+      float v = part[r][n];
+      v += __shfl_xor(v, 16, kWave);
+      v += __shfl_xor(v, 32, kWave);
+      out[r][n] = v;
+    }
+}
+
 }  // namespace dssel

@@ -65,6 +65,7 @@ static_assert(kMaxRows <= 32, "row tag must fit above the position bits");
 template <int R>
 struct ScoreShared {
   int32_t list[kPiece];
+  uint8_t rowbits[kPiece];  // mask row per query row: bit r = row r admits the element
   uint2 stage[kWaves][kWaveStage];  // (key, position | row << kRowShift)
   int P[kMaxRows];
   int64_t lim[kMaxRows];
@@ -92,8 +93,6 @@ struct PieceCtx {
   int32_t* cand_count;         // [R][kCountPad] of this layer
   uint64_t* cand;              // [R][stride] of this layer
   int64_t stride;
-  const uint32_t* mask_l;      // the layer's mask rows (kRowMask)
-  int64_t mask_row_stride;
 
   // Layer position of piece element e: contiguous pieces hold [off, off + cnt);
   // interleaved piece j of pn holds groups j, j + pn, j + 2 pn, ... of 16.
@@ -108,11 +107,10 @@ struct PieceCtx {
   }
 
   // With a mask row per query row, the union list also holds blocks that row
-  // r does not admit: test its own bit and limit.
+  // r does not admit: its own bit and limit, gathered at the piece's set-up
+  // (no global load inside the stream, whose loads then stay in flight).
   __device__ __forceinline__ bool row_admits(int r, int e) const {
-    const int b = sh->list[e];
-    const uint32_t word = mask_l[r * mask_row_stride + (b >> 5)];
-    return ((word >> (b & 31)) & 1u) && (int64_t)b < sh->lim[r];
+    return (sh->rowbits[e] >> r) & 1u;
   }
 
   // Stage the lanes' candidates: lane i offers (key, position pos of row r)
@@ -179,6 +177,9 @@ struct PieceCtx {
     write_out(start);
     wave_lds_sync();
     nst = 0;
+    // Rejoin the stream with nothing of this path in flight, so that the
+    // stream's own counter waits (for its prefetched key rows) stay partial.
+    __builtin_amdgcn_s_waitcnt(0);
   }
 };
 
@@ -190,6 +191,7 @@ struct PieceCtx {
 template <int R, int D, int NBUF>
 struct MfmaEngine {
   static constexpr int kRows = R, kBuffers = NBUF;
+  static constexpr bool kPairs = false;
   static constexpr int KC = D / 32;       // 32-column chunks of a key row
   static constexpr int S = (R + 3) / 4;   // MFMA row sets
   bf16x8_t a[S][KC];                      // A operand: q~ parts (row m = lane % 16)
@@ -214,16 +216,14 @@ struct MfmaEngine {
 
   template <int B>
   __device__ __forceinline__ void load(const PieceCtx<R>& t, const uint16_t* K, int64_t ldk, int g0) {
+    // Every lane loads (a lane past the piece's end re-reads the group's first
+    // row, whose score it never offers), so the stream has no divergent
+    // branch around its loads and the counter waits stay exact.
     const int lane = lane_id();
     const int e = g0 + (lane & 15);
-    if (t.valid(e)) {
-      const uint16_t* row = K + (int64_t)t.block_of(e) * ldk + 8 * (lane >> 4);
+    const uint16_t* row = K + (int64_t)t.block_of(t.valid(e) ? e : g0) * ldk + 8 * (lane >> 4);
 #pragma unroll
-      for (int cc = 0; cc < KC; ++cc) buf[B][cc] = load16(row + 32 * cc);
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < KC; ++cc) buf[B][cc] = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int cc = 0; cc < KC; ++cc) buf[B][cc] = load16(row + 32 * cc);
   }
 
   template <int B>
@@ -277,6 +277,7 @@ struct MfmaEngine {
 template <int R, int D, int NBUF>
 struct MfmaQ8Engine {
   static constexpr int kRows = R, kBuffers = NBUF;
+  static constexpr bool kPairs = false;
   static constexpr int KC = D / 32;       // 32-column groups of a key row
   static constexpr int S = (R + 3) / 4;   // MFMA row sets
   bf16x8_t a[S][KC];
@@ -311,21 +312,14 @@ struct MfmaQ8Engine {
   __device__ __forceinline__ void load(const PieceCtx<R>& t, const uint16_t*, int64_t, int g0) {
     const int lane = lane_id();
     const int e = g0 + (lane & 15);
-    if (t.valid(e)) {
-      const int64_t b = t.block_of(e);
-      const int8_t* row = codes_l + b * ldc + 8 * (lane >> 4);
+    const int64_t b = t.block_of(t.valid(e) ? e : g0);
+    const int8_t* row = codes_l + b * ldc + 8 * (lane >> 4);
 #pragma unroll
-      for (int cc = 0; cc < KC; ++cc) buf[B][cc] = *reinterpret_cast<const uint2*>(row + 32 * cc);
-      const uint16_t* sr = scales_l + b * lds;
+    for (int cc = 0; cc < KC; ++cc) buf[B][cc] = *reinterpret_cast<const uint2*>(row + 32 * cc);
+    const uint16_t* sr = scales_l + b * lds;
 #pragma unroll
-      for (int h = 0; h < (KC + 1) / 2; ++h)
-        sbuf[B][h] = (uint32_t)sr[2 * h] | (2 * h + 1 < KC ? (uint32_t)sr[2 * h + 1] << 16 : 0u);
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < KC; ++cc) buf[B][cc] = make_uint2(0u, 0u);
-#pragma unroll
-      for (int h = 0; h < (KC + 1) / 2; ++h) sbuf[B][h] = 0u;
-    }
+    for (int h = 0; h < (KC + 1) / 2; ++h)
+      sbuf[B][h] = (uint32_t)sr[2 * h] | (2 * h + 1 < KC ? (uint32_t)sr[2 * h + 1] << 16 : 0u);
   }
 
   template <int B>
@@ -380,52 +374,52 @@ struct MfmaQ8Engine {
 template <int R, int D, int NBUF>
 struct ReluEngine {
   static constexpr int kRows = R, kBuffers = NBUF;
+  static constexpr bool kPairs = true;  // two groups per buffer: each LDS fragment feeds 2 MFMAs
   static constexpr int KC = D / 32;
   static constexpr int S = (R + 3) / 4;
-  relu_u32x4_t buf[NBUF][1][KC];
+  relu_u32x4_t buf[NBUF][2][KC];
   ReluStage st;
 
   __device__ void init(const Call& c, int l, uint32_t* lds) {
     st = relu_stage_heads<R, D>(c, l, lds, threadIdx.x, kScoreThreads);
   }
 
+  // Groups ga and gb (both valid group starts) into buffer B.
   template <int B>
-  __device__ __forceinline__ void load(const PieceCtx<R>& t, const uint16_t* K, int64_t ldk, int g0) {
+  __device__ __forceinline__ void load2(const PieceCtx<R>& t, const uint16_t* K, int64_t ldk, int ga, int gb) {
     const int lane = lane_id();
-    const int e = g0 + (lane & 15);
-    if (t.valid(e)) {
-      const uint16_t* row = K + (int64_t)t.block_of(e) * ldk + 8 * (lane >> 4);
 #pragma unroll
-      for (int cc = 0; cc < KC; ++cc) buf[B][0][cc] = load16(row + 32 * cc);
-    } else {
+    for (int h = 0; h < 2; ++h) {
+      const int g0 = h ? gb : ga;
+      const int e = g0 + (lane & 15);
+      const uint16_t* row = K + (int64_t)t.block_of(t.valid(e) ? e : g0) * ldk + 8 * (lane >> 4);
 #pragma unroll
-      for (int cc = 0; cc < KC; ++cc) buf[B][0][cc] = relu_u32x4_t{0u, 0u, 0u, 0u};
+      for (int cc = 0; cc < KC; ++cc) buf[B][h][cc] = load16(row + 32 * cc);
     }
   }
 
   template <int B>
-  __device__ __forceinline__ void compute_emit(PieceCtx<R>& t, int g0) {
-    float sc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float o[1];
-      relu_row_scores<D, 1>(st, r, buf[B], o);
-      sc[r] = o[0];
-    }
+  __device__ __forceinline__ void compute_emit2(PieceCtx<R>& t, int ga, int gb) {
+    float o[R][2];
+    relu_all_rows<R, D, 2, (R * KC <= 32)>(st, buf[B], o);  // prefetch while it fits
     const int lane = lane_id();
-    const int e = g0 + (lane & 15), g = lane >> 4;
-    const int pos = t.pos_of(e);
-    const bool live = e < t.cnt;
+    const int g = lane >> 4;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      float v = sc[0];
+    for (int h = 0; h < 2; ++h) {
+      const int e = (h ? gb : ga) + (lane & 15);
+      const int pos = t.pos_of(e);
+      const bool live = e < t.cnt;
 #pragma unroll
-      for (int r = 1; r < R; ++r)
-        if (r == 4 * s + g) v = sc[r];
-      const uint32_t key = score_to_key(v);
-      bool ok = live && pos < lp[s] && key >= lf[s];
-      if (t.mode == kRowMask && ok) ok = t.row_admits(4 * s + g, e);
-      t.append(ok, key, pos, 4 * s + g);
+      for (int s = 0; s < S; ++s) {
+        float v = o[0][h];
+#pragma unroll
+        for (int r = 1; r < R; ++r)
+          if (r == 4 * s + g) v = o[r][h];
+        const uint32_t key = score_to_key(v);
+        bool ok = live && pos < lp[s] && key >= lf[s];
+        if (t.mode == kRowMask && ok) ok = t.row_admits(4 * s + g, e);
+        t.append(ok, key, pos, 4 * s + g);
+      }
     }
   }
 
@@ -446,6 +440,7 @@ struct ReluEngine {
 template <int R, int D, int NBUF>
 struct ValuEngine {
   static constexpr int kRows = R, kBuffers = NBUF;
+  static constexpr bool kPairs = false;
   static constexpr int LPR = D / 8;        // lanes per key row
   static constexpr int RPI = kWave / LPR;  // key rows per load instruction
   static constexpr int U = kGroup / RPI;   // load instructions per group
@@ -469,8 +464,7 @@ struct ValuEngine {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int e = g0 + u * RPI + rr;
-      buf[B][u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (t.valid(e)) buf[B][u] = load16(K + (int64_t)t.block_of(e) * ldk + slice * 8);
+      buf[B][u] = load16(K + (int64_t)t.block_of(t.valid(e) ? e : g0) * ldk + slice * 8);
     }
   }
 
@@ -516,6 +510,10 @@ struct ValuEngine {
 // Runs the wave's groups g0, g0 + step, ... < cnt through a ring of NBUF load
 // buffers: the loads for group j + NBUF - 1 are issued before group j is
 // computed, so NBUF - 1 groups of key rows are in flight behind the arithmetic.
+// The loads are issued unconditionally (a prefetch past the last group re-reads
+// the group being computed, an L2 hit): with no branch around them the
+// compiler's counter waits stay exact, and a computing group waits only for
+// its own rows, never for the younger groups' loads.
 template <int NBUF, class Engine, int J>
 __device__ __forceinline__ void ring_step(Engine& eng, PieceCtx<Engine::kRows>& pc,
                                           const uint16_t* K, int64_t ldk, int g, int step) {
@@ -523,7 +521,7 @@ __device__ __forceinline__ void ring_step(Engine& eng, PieceCtx<Engine::kRows>& 
     const int gj = g + J * step;
     if (gj >= pc.cnt) return;
     const int gl = gj + (NBUF - 1) * step;
-    if (gl < pc.cnt) eng.template load<(J + NBUF - 1) % NBUF>(pc, K, ldk, gl);
+    eng.template load<(J + NBUF - 1) % NBUF>(pc, K, ldk, gl < pc.cnt ? gl : gj);
     eng.template compute_emit<J>(pc, gj);
     ring_step<NBUF, Engine, J + 1>(eng, pc, K, ldk, g, step);
   }
@@ -534,7 +532,7 @@ __device__ __forceinline__ void ring_prologue(Engine& eng, PieceCtx<Engine::kRow
                                               const uint16_t* K, int64_t ldk, int g0, int step) {
   if constexpr (J < NBUF - 1) {
     const int gj = g0 + J * step;
-    if (gj < pc.cnt) eng.template load<J>(pc, K, ldk, gj);
+    eng.template load<J>(pc, K, ldk, gj < pc.cnt ? gj : g0);
     ring_prologue<NBUF, Engine, J + 1>(eng, pc, K, ldk, g0, step);
   }
 }
@@ -542,8 +540,46 @@ __device__ __forceinline__ void ring_prologue(Engine& eng, PieceCtx<Engine::kRow
 template <int NBUF, class Engine>
 __device__ __forceinline__ void stream_piece(Engine& eng, PieceCtx<Engine::kRows>& pc,
                                              const uint16_t* K, int64_t ldk, int g0, int step) {
+  if (g0 >= pc.cnt) return;  // this wave has no group
   ring_prologue<NBUF, Engine, 0>(eng, pc, K, ldk, g0, step);
   for (int g = g0; g < pc.cnt; g += NBUF * step) ring_step<NBUF, Engine, 0>(eng, pc, K, ldk, g, step);
+}
+
+// The same ring for an engine that takes two groups per buffer: pair p is
+// groups g0 + 2 p step and g0 + (2 p + 1) step.  A group past the piece's end
+// re-reads a valid group (never offered), so the loads stay unconditional.
+template <int NBUF, class Engine, int J>
+__device__ __forceinline__ void pair_step(Engine& eng, PieceCtx<Engine::kRows>& pc,
+                                          const uint16_t* K, int64_t ldk, int g, int step) {
+  if constexpr (J < NBUF) {
+    const int pstep = 2 * step;
+    const int gj = g + J * pstep;
+    if (gj >= pc.cnt) return;
+    const int gl = gj + (NBUF - 1) * pstep;
+    const int la = gl < pc.cnt ? gl : gj;
+    eng.template load2<(J + NBUF - 1) % NBUF>(pc, K, ldk, la, la + step < pc.cnt ? la + step : la);
+    eng.template compute_emit2<J>(pc, gj, gj + step);
+    pair_step<NBUF, Engine, J + 1>(eng, pc, K, ldk, g, step);
+  }
+}
+
+template <int NBUF, class Engine, int J>
+__device__ __forceinline__ void pair_prologue(Engine& eng, PieceCtx<Engine::kRows>& pc,
+                                              const uint16_t* K, int64_t ldk, int g0, int step) {
+  if constexpr (J < NBUF - 1) {
+    const int ga = g0 + J * 2 * step;
+    const int la = ga < pc.cnt ? ga : g0;
+    eng.template load2<J>(pc, K, ldk, la, la + step < pc.cnt ? la + step : la);
+    pair_prologue<NBUF, Engine, J + 1>(eng, pc, K, ldk, g0, step);
+  }
+}
+
+template <int NBUF, class Engine>
+__device__ __forceinline__ void stream_piece_pairs(Engine& eng, PieceCtx<Engine::kRows>& pc,
+                                                   const uint16_t* K, int64_t ldk, int g0, int step) {
+  if (g0 >= pc.cnt) return;
+  pair_prologue<NBUF, Engine, 0>(eng, pc, K, ldk, g0, step);
+  for (int g = g0; g < pc.cnt; g += NBUF * 2 * step) pair_step<NBUF, Engine, 0>(eng, pc, K, ldk, g, step);
 }
 
 // Which piece this workgroup streams.  Every layer's admitted positions are
@@ -643,6 +679,29 @@ __device__ __forceinline__ void score_body(const Call& c, uint32_t* relu_lds) {
       const int i = tid + u * kScoreThreads;
       if (i < pc.cnt) sh.list[i] = v[u];
     }
+    if (c.mode == kRowMask) {
+      const uint32_t* mask_l = c.mask + (int64_t)sl * c.mask_layer_stride;
+      int64_t lim[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t x = c.limit ? (int64_t)c.limit[(int64_t)sl * R + r] : N;
+        lim[r] = x < 0 ? 0 : (x > N ? N : x);
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int i = tid + u * kScoreThreads;
+        if (i < pc.cnt) {
+          const int b = v[u];
+          uint32_t bits = 0;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint32_t word = mask_l[r * c.mask_row_stride + (b >> 5)];
+            bits |= (((word >> (b & 31)) & 1u) && (int64_t)b < lim[r] ? 1u : 0u) << r;
+          }
+          sh.rowbits[i] = (uint8_t)bits;
+        }
+      }
+    }
   }
   if (tid < kMaxRows) {
     sh.P[tid] = tid < R ? (c.mode == kRowMask ? nl : counts[tid]) : 0;
@@ -662,10 +721,11 @@ __device__ __forceinline__ void score_body(const Call& c, uint32_t* relu_lds) {
   pc.cand_count = c.cand_count + (int64_t)sl * R * kCountPad;
   pc.cand = c.cand + (int64_t)sl * R * c.cand_stride;
   pc.stride = c.cand_stride;
-  pc.mask_l = c.mask ? c.mask + (int64_t)sl * c.mask_layer_stride : nullptr;
-  pc.mask_row_stride = c.mask_row_stride;
-  stream_piece<Engine::kBuffers>(eng, pc, c.keys ? c.keys + (int64_t)sl * c.key_layer_stride : nullptr,
-                                 c.ldk, wave * kGroup, kWaves * kGroup);
+  const uint16_t* K = c.keys ? c.keys + (int64_t)sl * c.key_layer_stride : nullptr;
+  if constexpr (Engine::kPairs)
+    stream_piece_pairs<Engine::kBuffers>(eng, pc, K, c.ldk, wave * kGroup, kWaves * kGroup);
+  else
+    stream_piece<Engine::kBuffers>(eng, pc, K, c.ldk, wave * kGroup, kWaves * kGroup);
   // End of the piece: one counter update per row for the whole workgroup.
   const int lane = lane_id();
   const int mine = pc.count_rows();  // lane r: this wave's staged entries of row r
@@ -685,6 +745,11 @@ __device__ __forceinline__ void score_body(const Call& c, uint32_t* relu_lds) {
   }
   pc.write_out(start);
 }
+
+// Load buffers per wave: two groups of key rows in flight; one at d = 256,
+// where a third buffer of 16-byte bf16 chunks (32 registers) does not fit.
+template <int D>
+constexpr int kRing = D >= 256 ? 2 : 3;
 
 // The MFMA kernel is held to at least W waves per SIMD: 4 (128 registers, 16
 // waves per compute unit: the memory parallelism the stream needs) at
@@ -707,13 +772,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel_valu(Call c) {
 template <int R, int D>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel_relu(Call c) {
   __shared__ uint32_t relu_lds[kReluStageBytes / 4];
-  score_body<R, D, ReluEngine<R, D, 3>>(c, relu_lds);
+  score_body<R, D, ReluEngine<R, D, kRing<D>>>(c, relu_lds);
 }
-
-// Load buffers per wave: two groups of key rows in flight; one at d = 256,
-// where a third buffer of 16-byte bf16 chunks (32 registers) does not fit.
-template <int D>
-constexpr int kRing = D >= 256 ? 2 : 3;
 
 template <int R, int D>
 hipError_t launch_rd(const Call& c, dim3 grid, hipStream_t s) {
