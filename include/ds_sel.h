@@ -237,6 +237,38 @@ typedef struct {
 
 int ds_sel_quantize_q8(const ds_sel_quantize_args* a, void* hip_stream);
 
+/* Serial decode: the layers of `a` one after another, each layer's query
+ * depending on the previous layer's selection (page "DeepSeek V4.1F Q4 on M3
+ * Ultra with native DSpark MTP (40tps / 800tps)", paragraph "Decode": the
+ * layers run one after another and the per-dispatch cost is what to remove).
+ * The model that links real layers is outside this library; its stand-in is
+ * a rotation of the next layer's query heads by this layer's best block:
+ *   layer 0 selects with q[0]; for l >= 1, row r selects with
+ *   q_l[r][h] = q[l][r][(h + s) mod H],  s = idx[l-1][r][0] mod H
+ *   (s = 0 when layer l-1 selected nothing for the row, idx -1).
+ * `a` is an ordinary call over L layers (same rules and capacity checks);
+ * q_work is caller-owned device memory, bf16 [L][R][H][d], 16-byte aligned
+ * (may be NULL when L == 1): layer l >= 1's rotated query is written to its
+ * slot l and read from there; slot 0 is not touched.  Outputs are those of
+ * ds_sel_score_select for every layer.  Enqueued on `hip_stream` as 4 L - 1
+ * launches (the chain's three per layer and the rotation between layers). */
+int ds_sel_decode(ds_sel* h, const ds_sel_args* a, void* q_work, void* hip_stream);
+
+/* The same serial decode captured once into a HIP graph, so that a decode
+ * step is one graph launch instead of 4 L - 1 kernel launches.  The plan
+ * records the pointers of `a` and q_work and the handle's scratch: the caller
+ * keeps them alive and unchanged in place (their contents may change between
+ * launches: every launch reads them afresh), and destroys the plan before the
+ * handle.  `hip_stream` must be a created stream (the legacy null stream
+ * cannot be captured); nothing is executed at create.  Launches on one plan,
+ * and calls on its handle, must be ordered on one stream.
+ * DS_SEL_E_HIP when capture or instantiation fails (no plan is returned). */
+typedef struct ds_sel_plan ds_sel_plan;
+int ds_sel_decode_plan_create(ds_sel* h, const ds_sel_args* a, void* q_work, void* hip_stream,
+                              ds_sel_plan** out);
+int ds_sel_decode_plan_launch(ds_sel_plan* p, void* hip_stream);
+void ds_sel_decode_plan_destroy(ds_sel_plan* p);  /* NULL is a no-op */
+
 /* Attention over a selection -- the step that consumes it (page "DeepSeek
  * V4.1F Q4 on M3 Ultra with native DSpark MTP (40tps / 800tps)", paragraph
  * "Decode at depth": each layer's compressed attention works on the blocks

@@ -151,6 +151,38 @@ def select(q, w, keys, k, mask=None, limit=None, lib=None, score="linear"):
     return idx, scores, count
 
 
+def decode_serial(q, w, keys, k, mask=None, limit=None, lib=None, score="linear"):
+    """Serial decode over the layers (each layer's query depends on the one before).
+
+    The pages' layers feed each other through the model (page "DeepSeek V4.1F
+    Q4 on M3 Ultra with native DSpark MTP (40tps / 800tps)", paragraph
+    "Decode"); the model is not part of this library, so a stand-in step links
+    the layers: layer 0 selects with q[0]; for l >= 1, row r selects with its
+    query heads rotated by its predecessor's best block,
+        q_l[r][h] = q[l][r][(h + s) mod H],  s = idx[l-1][r][0] mod H
+    (s = 0 when layer l-1 selected nothing for row r).  Inputs and outputs as
+    select(); returns (idx, score, count) for every layer.
+    """
+    q = _c(q, np.uint16)
+    L, R, H, _ = q.shape
+    idx = np.empty((L, R, k), np.int32)
+    scores = np.empty((L, R, k), np.float32)
+    count = np.empty((L, R), np.int32)
+    lib = lib or load()
+    cur = q[0:1]
+    for l in range(L):
+        if l > 0:
+            cur = np.empty_like(q[l:l + 1])
+            for r in range(R):
+                s = int(idx[l - 1, r, 0]) % H if count[l - 1, r] > 0 else 0
+                cur[0, r] = np.roll(q[l, r], -s, axis=0)
+        sl = slice(l, l + 1)
+        out = select(cur, w[sl], keys[sl], k, None if mask is None else mask[sl],
+                     None if limit is None else limit[sl], lib=lib, score=score)
+        idx[l], scores[l], count[l] = out[0][0], out[1][0], out[2][0]
+    return idx, scores, count
+
+
 def _scored(lib, name, score):
     if score == "linear":
         return getattr(lib, name)

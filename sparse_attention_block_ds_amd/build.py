@@ -21,7 +21,7 @@ LIBRARY = os.path.join(PKG, "libdssel.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["ds_sel.cpp", "prep.hip", "score.hip", "select.hip", "attend.hip", "calibrate.hip", "quantize.hip"]
+SOURCES = ["ds_sel.cpp", "prep.hip", "score.hip", "select.hip", "attend.hip", "calibrate.hip", "quantize.hip", "decode.hip"]
 
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -383,6 +383,122 @@ int ds_sel_poison_scratch(ds_sel* h, int32_t byte, void* hip_stream) {
   });
 }
 
+// ---------------------------------------------------------------- serial decode
+namespace {
+
+// The layers of `a` one after another, each a one-layer call of the chain,
+// with the stand-in step between them writing layer l + 1's query into q_work.
+int enqueue_decode(const Target& t, const ds_sel_args* a, void* q_work, hipStream_t stream) {
+  const int64_t L = a->layers, R = a->rows, H = a->heads, D = a->dim, k = a->k;
+  const uint16_t* q = static_cast<const uint16_t*>(a->q);
+  uint16_t* qw = static_cast<uint16_t*>(q_work);
+  for (int64_t l = 0; l < L; ++l) {
+    ds_sel_args al = *a;
+    al.layers = 1;
+    al.q = l == 0 ? a->q : static_cast<const void*>(qw + l * R * H * D);
+    al.w = static_cast<const uint16_t*>(a->w) + l * R * H;
+    if (a->keys) al.keys = static_cast<const uint16_t*>(a->keys) + l * a->key_layer_stride;
+    if (a->mask) al.mask = a->mask + l * a->mask_layer_stride;
+    if (a->limit) al.limit = a->limit + l * R;
+    al.out_idx = a->out_idx + l * R * k;
+    al.out_score = a->out_score + l * R * k;
+    if (a->out_count) al.out_count = a->out_count + l * R;
+    const int rc = enqueue(t, &al, stream, nullptr);
+    if (rc != DS_SEL_OK) return rc;
+    if (l + 1 < L) {
+      dssel::RotateCall rcall{};
+      rcall.rows = (int32_t)R;
+      rcall.heads = (int32_t)H;
+      rcall.dim = (int32_t)D;
+      rcall.k = (int32_t)k;
+      rcall.q_next = q + (l + 1) * R * H * D;
+      rcall.idx = al.out_idx;
+      rcall.q_out = qw + (l + 1) * R * H * D;
+      const int e = with_device(t.device, [&]() {
+        return dssel::launch_rotate(rcall, stream) == hipSuccess ? (int)DS_SEL_OK : (int)DS_SEL_E_HIP;
+      });
+      if (e != DS_SEL_OK) return e;
+    }
+  }
+  return DS_SEL_OK;
+}
+
+int check_decode(const ds_sel* h, const ds_sel_args* a, const void* q_work) {
+  if (!h) return DS_SEL_E_INVALID;
+  const int rc = check_args(h->lim, a);
+  if (rc != DS_SEL_OK) return rc;
+  if (a->layers > 1 && (!q_work || !aligned(q_work, 16))) return DS_SEL_E_INVALID;
+  return DS_SEL_OK;
+}
+
+}  // namespace
+
+struct ds_sel_plan {
+  int device = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipEvent_t done = nullptr;  // the handle's: a launch is a call on the handle
+};
+
+int ds_sel_decode(ds_sel* h, const ds_sel_args* a, void* q_work, void* hip_stream) {
+  const int rc = check_decode(h, a, q_work);
+  if (rc != DS_SEL_OK) return rc;
+  return enqueue_decode(handle_target(h), a, q_work, static_cast<hipStream_t>(hip_stream));
+}
+
+int ds_sel_decode_plan_create(ds_sel* h, const ds_sel_args* a, void* q_work, void* hip_stream,
+                              ds_sel_plan** out) {
+  if (!out) return DS_SEL_E_INVALID;
+  *out = nullptr;
+  const int rc = check_decode(h, a, q_work);
+  if (rc != DS_SEL_OK) return rc;
+  if (!hip_stream) return DS_SEL_E_INVALID;  // the legacy null stream cannot be captured
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  ds_sel_plan* p = new (std::nothrow) ds_sel_plan;
+  if (!p) return DS_SEL_E_NOMEM;
+  p->device = h->lim.device;
+  p->done = h->done;
+  const int e = with_device(p->device, [&]() {
+    if (hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal) != hipSuccess) return (int)DS_SEL_E_HIP;
+    const int erc = enqueue_decode(handle_target(h), a, q_work, stream);
+    hipGraph_t g = nullptr;
+    const hipError_t end = hipStreamEndCapture(stream, &g);
+    if (erc != DS_SEL_OK || end != hipSuccess || !g) {
+      if (g) (void)hipGraphDestroy(g);
+      (void)hipGetLastError();
+      return erc != DS_SEL_OK ? erc : (int)DS_SEL_E_HIP;
+    }
+    p->graph = g;
+    if (hipGraphInstantiate(&p->exec, g, nullptr, nullptr, 0) != hipSuccess) return (int)DS_SEL_E_HIP;
+    return (int)DS_SEL_OK;
+  });
+  if (e != DS_SEL_OK) {
+    ds_sel_decode_plan_destroy(p);
+    return e;
+  }
+  *out = p;
+  return DS_SEL_OK;
+}
+
+int ds_sel_decode_plan_launch(ds_sel_plan* p, void* hip_stream) {
+  if (!p || !p->exec) return DS_SEL_E_INVALID;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  return with_device(p->device, [&]() {
+    if (hipGraphLaunch(p->exec, stream) != hipSuccess) return (int)DS_SEL_E_HIP;
+    return mark_done(p->done, stream);
+  });
+}
+
+void ds_sel_decode_plan_destroy(ds_sel_plan* p) {
+  if (!p) return;
+  with_device(p->device, [&]() {
+    if (p->exec) (void)hipGraphExecDestroy(p->exec);
+    if (p->graph) (void)hipGraphDestroy(p->graph);
+    return (int)DS_SEL_OK;
+  });
+  delete p;
+}
+
 int ds_sel_score_select_q8(ds_sel* h, const ds_sel_args* a, const ds_sel_q8_keys* k8, void* hip_stream,
                            void* const events[4]) {
   if (!h || !k8) return DS_SEL_E_INVALID;

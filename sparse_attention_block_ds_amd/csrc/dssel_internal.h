@@ -138,6 +138,16 @@ struct AttendCall {
 hipError_t launch_attend(const AttendCall& c, hipStream_t stream);
 
 // Quantising bf16 key rows into the 8-bit stream (ds_sel_quantize_q8).
+// The serial decode's step between layers: layer l + 1's query heads rotated
+// by layer l's best block per row (decode.hip).
+struct RotateCall {
+  int32_t rows, heads, dim, k;
+  const uint16_t* q_next;  // bf16 [R][H][d]: layer l + 1's base query
+  const int32_t* idx;      // int32 [R][k]: layer l's selection
+  uint16_t* q_out;         // bf16 [R][H][d]: layer l + 1's query
+};
+hipError_t launch_rotate(const RotateCall& c, hipStream_t stream);
+
 struct QuantizeCall {
   int32_t layers, dim;
   int64_t blocks;

@@ -30,7 +30,8 @@ EXPORTED = ("ds_sel_create", "ds_sel_score_select", "ds_sel_score_select_profile
             "ds_sel_attend", "ds_sel_check_attend_args", "ds_sel_calibrate",
             "ds_sel_score_select_noalloc", "ds_sel_noalloc_scratch_bytes",
             "ds_sel_score_select_q8", "ds_sel_check_args_q8", "ds_sel_quantize_q8",
-            "ds_sel_poison_scratch")
+            "ds_sel_poison_scratch", "ds_sel_decode", "ds_sel_decode_plan_create",
+            "ds_sel_decode_plan_launch", "ds_sel_decode_plan_destroy")
 
 DS_SEL_CALIB_EMPTY = 0
 DS_SEL_CALIB_READ = 1
@@ -147,6 +148,15 @@ def load_library(path: Optional[str] = None):
     lib.ds_sel_check_args_q8.restype = ctypes.c_int
     lib.ds_sel_quantize_q8.argtypes = [P(QuantizeArgs), ctypes.c_void_p]
     lib.ds_sel_quantize_q8.restype = ctypes.c_int
+    lib.ds_sel_decode.argtypes = [ctypes.c_void_p, P(Args), ctypes.c_void_p, ctypes.c_void_p]
+    lib.ds_sel_decode.restype = ctypes.c_int
+    lib.ds_sel_decode_plan_create.argtypes = [ctypes.c_void_p, P(Args), ctypes.c_void_p, ctypes.c_void_p,
+                                              P(ctypes.c_void_p)]
+    lib.ds_sel_decode_plan_create.restype = ctypes.c_int
+    lib.ds_sel_decode_plan_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.ds_sel_decode_plan_launch.restype = ctypes.c_int
+    lib.ds_sel_decode_plan_destroy.argtypes = [ctypes.c_void_p]
+    lib.ds_sel_decode_plan_destroy.restype = None
     lib.ds_sel_poison_scratch.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     lib.ds_sel_poison_scratch.restype = ctypes.c_int
     lib.ds_sel_status_string.argtypes = [ctypes.c_int]
@@ -437,6 +447,50 @@ class Selector:
         if rc != DS_SEL_OK:
             raise DsSelError(rc, "ds_sel_poison_scratch")
 
+    def _decode_args(self, q, w, keys, k, mask, limit, q_work, out):
+        torch = self._torch
+        check_select_tensors(q, w, keys, k, mask, limit, out, torch.device("cuda", self.device))
+        L, R = q.shape[0], q.shape[1]
+        if out is None:
+            out = (torch.empty((L, R, k), dtype=torch.int32, device=q.device),
+                   torch.empty((L, R, k), dtype=torch.float32, device=q.device),
+                   torch.empty((L, R), dtype=torch.int32, device=q.device))
+        if q_work is None:
+            q_work = torch.empty_like(q)
+        _require(q_work.dtype == torch.bfloat16 and q_work.shape == q.shape and q_work.is_contiguous()
+                 and q_work.device == q.device, "q_work must be a contiguous bf16 tensor shaped like q")
+        return make_args(q, w, keys, k, mask, limit, *out), q_work, out
+
+    def decode(self, q, w, keys, k, mask=None, limit=None, q_work=None, out=None, stream=None):
+        """Serial decode over the L layers (ds_sel_decode): layer l >= 1 selects
+        with its query heads rotated by layer l-1's best block per row; q_work
+        (bf16 like q) receives those queries.  Returns (idx, score, count)."""
+        torch = self._torch
+        a, q_work, out = self._decode_args(q, w, keys, k, mask, limit, q_work, out)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        rc = self.lib.ds_sel_decode(self.handle, ctypes.byref(a), _ptr(q_work), ctypes.c_void_p(handle))
+        if rc != DS_SEL_OK:
+            raise DsSelError(rc, "ds_sel_decode")
+        return out
+
+    def decode_plan(self, q, w, keys, k, mask=None, limit=None, q_work=None, out=None, stream=None):
+        """The serial decode captured into a HIP graph (ds_sel_decode_plan_create)
+        on `stream` (a created torch.cuda.Stream, not the null stream).  Returns
+        a DecodePlan whose launch() replays it; the tensors must stay alive."""
+        torch = self._torch
+        a, q_work, out = self._decode_args(q, w, keys, k, mask, limit, q_work, out)
+        if stream is None:
+            raise ValueError("decode_plan needs a created stream to capture on")
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        p = ctypes.c_void_p()
+        rc = self.lib.ds_sel_decode_plan_create(self.handle, ctypes.byref(a), _ptr(q_work),
+                                                ctypes.c_void_p(handle), ctypes.byref(p))
+        if rc != DS_SEL_OK:
+            raise DsSelError(rc, "ds_sel_decode_plan_create")
+        return DecodePlan(self, p, (q, w, keys, mask, limit, q_work) + tuple(out), out)
+
     def score_select_q8(self, q, w, codes, scales, k, mask=None, limit=None, out=None,
                         stream=None, events=None):
         """score_select over the 8-bit key stream (ds_sel_score_select_q8):
@@ -489,6 +543,31 @@ class Selector:
         if rc != DS_SEL_OK:
             raise DsSelError(rc, "ds_sel_attend")
         return out
+
+
+class DecodePlan:
+    """A captured serial decode; holds its tensors so they outlive the graph."""
+
+    def __init__(self, selector, handle, keep, out):
+        self.selector, self.handle, self._keep, self.out = selector, handle, keep, out
+
+    def launch(self, stream):
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        rc = self.selector.lib.ds_sel_decode_plan_launch(self.handle, ctypes.c_void_p(handle))
+        if rc != DS_SEL_OK:
+            raise DsSelError(rc, "ds_sel_decode_plan_launch")
+        return self.out
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.selector.lib.ds_sel_decode_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def upload(problem, device="cuda"):

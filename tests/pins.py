@@ -446,6 +446,39 @@ def check_select_relu(lib):
         np.testing.assert_array_equal(rel, np.where(lin > 0, lin, np.float32(0.0)))
 
 
+# ------------------------------------------------------------------ serial decode
+def check_decode_serial(lib):
+    """Serial decode against brute force: each layer's best block found by
+    counting over int64 exact scores, the next layer's heads rotated by hand,
+    its scores recomputed exactly; and with one head the rotation is the
+    identity, so the result equals the batched selection bit for bit."""
+    p = wl.make_custom(3, 2, 8, 64, 600, 40, seed=95, values="int3", mask_p=0.7,
+                       mask_shared=False)
+    idx, score, count = oracle.decode_serial(p.q, p.w, p.keys, p.k, p.mask, p.limit, lib=lib)
+    qf = wl.bf16_bits_to_f32(p.q).astype(np.int64)
+    wf = wl.bf16_bits_to_f32(p.w).astype(np.int64)
+    kf = wl.bf16_bits_to_f32(p.keys).astype(np.int64)
+    adm = admitted_mask(p)
+    H = p.heads
+    shifts = np.zeros(p.rows, np.int64)
+    for l in range(p.layers):
+        for r in range(p.rows):
+            qr = np.array([qf[l, r, (h + shifts[r]) % H] for h in range(H)])   # heads by hand
+            exact = np.array([sum(int(wf[l, r, h]) * int(qr[h] @ kf[l, b]) for h in range(H))
+                              for b in range(p.blocks)], np.int64)
+            e_idx, e_val, e_cnt = brute_force_topk(exact, adm[l, r], p.k)
+            assert count[l, r] == e_cnt
+            np.testing.assert_array_equal(idx[l, r], e_idx)
+            np.testing.assert_array_equal(score[l, r], e_val.astype(np.float32))
+        shifts = np.array([idx[l, r, 0] % H if count[l, r] > 0 else 0 for r in range(p.rows)])
+    assert (shifts != 0).any(), "the rotation must be exercised"
+    p1 = wl.make_custom(4, 3, 1, 64, 500, 30, seed=96, values="int3", mask_p=0.5)
+    a = oracle.decode_serial(p1.q, p1.w, p1.keys, p1.k, p1.mask, p1.limit, lib=lib)
+    b = oracle.select(p1.q, p1.w, p1.keys, p1.k, p1.mask, p1.limit, lib=lib)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
 # ------------------------------------------------------------------ attention
 def _bits(a):
     return wl.f32_to_bf16_bits(np.asarray(a, np.float32))
@@ -557,6 +590,7 @@ def all_pins(lib, include_slow=False):
     check_quantize_q8(lib)
     check_select_q8(lib)
     check_select_relu(lib)
+    check_decode_serial(lib)
     check_attend(lib)
     if include_slow:
         check_exact_integer(wl.make("tiny"), lib)

@@ -411,3 +411,15 @@ def test_head_relu_supported_where_the_heads_fit(lib):
     assert sel.selector_flags("mfma", "relu") == relu
     with pytest.raises(ValueError):
         sel.selector_flags("mfma", "tanh")
+
+
+def test_decode_entry_points_reject_without_a_handle(lib):
+    a = _args()
+    assert lib.ds_sel_decode(None, ctypes.byref(a), None, None) == sel.DS_SEL_E_INVALID
+    p = ctypes.c_void_p(77)
+    assert lib.ds_sel_decode_plan_create(None, ctypes.byref(a), None, None, ctypes.byref(p)) == \
+        sel.DS_SEL_E_INVALID
+    assert not p.value
+    assert lib.ds_sel_decode_plan_create(None, ctypes.byref(a), None, None, None) == sel.DS_SEL_E_INVALID
+    assert lib.ds_sel_decode_plan_launch(None, None) == sel.DS_SEL_E_INVALID
+    lib.ds_sel_decode_plan_destroy(None)
