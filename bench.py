@@ -34,7 +34,10 @@ Prints one JSON line on stdout.  Besides the contract's keys it carries:
                  codes, one fp16 scale per 32): throughput and its own
                  roofline on that stream's algorithmic bytes (not part of value);
   relu           the same workload under the per-head ReLU score: the score
-                 kernel's flops against the bf16 MFMA peak (not part of value).
+                 kernel's flops against the bf16 MFMA peak (not part of value);
+  decode         the 300k x43 and sweep configs decoded serially (each layer's
+                 query depends on the previous layer's selection): per-layer
+                 latency of eager launches and of one captured graph replay.
 """
 from __future__ import annotations
 
@@ -87,6 +90,7 @@ def parse():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the calibration launches")
     ap.add_argument("--no-q8", action="store_true", help="skip the 8-bit key stream leg")
     ap.add_argument("--no-relu", action="store_true", help="skip the per-head ReLU score leg")
+    ap.add_argument("--no-decode", action="store_true", help="skip the serial decode legs")
     ap.add_argument("--calls", type=int, default=200,
                     help="event-bracketed calls per single-call leg")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -559,6 +563,82 @@ def relu_leg(p, stream, steps, warmup):
     }
 
 
+def decode_leg(name, stream, reps):
+    """Serial decode over the workload's layers (each layer's query depends on
+    the previous layer's selection): per-layer device time of eager launches
+    (4 L - 1 kernels enqueued one by one) and of the captured graph replay,
+    median / p10 / p90 over `reps` decodes, HIP events on the launch stream.
+    Two input copies alternate.  Sampled layers are checked against the oracle
+    given the GPU's own previous layer (bit-exact on integer inputs)."""
+    import numpy as np
+    import torch
+    import oracle
+    from sparse_attention_block_ds_amd import selector as sel
+    from sparse_attention_block_ds_amd import workloads as wl
+    p = wl.make(name)
+    L, R, H = p.layers, p.rows, p.heads
+    s = sel.Selector(max_layers=L, max_rows=R, max_heads=H, max_dim=p.dim, max_blocks=p.blocks,
+                     max_k=p.k, device=0)
+    cap = torch.cuda.Stream()
+    sets = []
+    for _ in range(2):
+        q, w, keys, mask, limit = sel.upload(p, "cuda:0")
+        qw = torch.empty_like(q)
+        out = (torch.empty((L, R, p.k), dtype=torch.int32, device="cuda:0"),
+               torch.empty((L, R, p.k), dtype=torch.float32, device="cuda:0"),
+               torch.empty((L, R), dtype=torch.int32, device="cuda:0"))
+        sets.append((q, w, keys, mask, limit, qw, out))
+    plans = [s.decode_plan(q, w, keys, p.k, mask, limit, q_work=qw, out=out, stream=cap)
+             for q, w, keys, mask, limit, qw, out in sets]
+
+    def timed(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        with torch.cuda.stream(cap):
+            for i in range(3):
+                fn(i)
+            for i, (a, b) in enumerate(evs):
+                a.record(cap)
+                fn(i)
+                b.record(cap)
+        torch.cuda.synchronize()
+        return pct([a.elapsed_time(b) * 1000.0 / L for a, b in evs])
+
+    def eager(i):
+        q, w, keys, mask, limit, qw, out = sets[i % 2]
+        s.decode(q, w, keys, p.k, mask, limit, q_work=qw, out=out, stream=cap)
+
+    eager_us = timed(eager)
+    graph_us = timed(lambda i: plans[i % 2].launch(cap))
+    # the last replay used set (reps - 1) % 2
+    idx, score, count = (t.cpu().numpy() for t in sets[(reps - 1) % 2][6])
+    bad = 0
+    checked = sorted({1, L // 2, L - 1} if L > 1 else {0})
+    lib = oracle.load()
+    for l in checked:
+        ql = p.q[l:l + 1].copy()
+        if l > 0:
+            for r in range(R):
+                sh = int(idx[l - 1, r, 0]) % H if count[l - 1, r] > 0 else 0
+                ql[0, r] = np.roll(p.q[l, r], -sh, axis=0)
+        for r in range(R):
+            sub = _sub_problem(wl.Problem("layer", p.k, np.concatenate([p.q[:l], ql, p.q[l + 1:]]), p.w,
+                                          p.keys, p.mask, p.limit, p.integer_valued), l, r)
+            ora = oracle.select(sub.q, sub.w, sub.keys, sub.k, sub.mask, sub.limit, lib=lib)
+            bad += 0 if _accept(p, sub, (idx, score, count), l, r, ora, lib) else 1
+    for pl in plans:
+        pl.close()
+    s.close()
+    if bad:
+        log(f"[bench] PARITY FAILURE in the {name} decode leg: {bad} selections")
+        sys.exit(3)
+    return {"workload": WORKLOADS[name] + ", layers serially dependent", "layers": L,
+            "eager_us_per_layer": eager_us, "graph_us_per_layer": graph_us,
+            "launches_per_decode": 4 * L - 1,
+            "parity": f"layers {checked} x {R} rows vs the oracle given the GPU's previous layer "
+                      + ("bit-exact" if p.integer_valued else "(tolerance + set rule)")}
+
+
 def attend_leg(run, steps):
     """Attention over the last step's selection (64 query heads per row, bf16 q
     and values drawn on the device from a fixed seed), timed with HIP events on
@@ -696,6 +776,15 @@ def main():
             relu = {"skipped": str(e)}
         torch.cuda.empty_cache()
 
+    decode = None
+    if not args.no_decode and args.workload == "sweep":
+        decode = {}
+        for name in ("300k_x43", "sweep"):
+            decode[name] = decode_leg(name, stream, 20)
+            log(f"[bench] decode {name}: eager {decode[name]['eager_us_per_layer']['median']:.1f} us, "
+                f"graph {decode[name]['graph_us_per_layer']['median']:.1f} us per layer")
+            torch.cuda.empty_cache()
+
     q8 = None
     if not args.no_q8 and p.dim % 32 == 0:
         q8 = q8_leg(p, stream, args.steps, args.warmup)
@@ -743,6 +832,7 @@ def main():
         "attend": attend,
         "q8": q8,
         "relu": relu,
+        "decode": decode,
     }
     print(json.dumps(line), flush=True)
 
