@@ -58,7 +58,7 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 // LDS words: the gathered words (at most 2 NT) with a run of zero padding,
 // then the best m in order (m <= k <= DS_SEL_MAX_K = 2048).
 constexpr int kGatherMax = 2048 + kGatherSlack;  // the most words gathered: k <= 2048, plus slack
-constexpr int kGatherCap = kGatherMax + kRun;
+constexpr int kGatherCap = (kGatherMax + kRun + 8 * kRun - 1) / (8 * kRun) * (8 * kRun);  // whole groups of 8 runs
 constexpr int kOrderedCap = 2048;
 
 // Everything that depends on the workgroup size NT (threads per row).
@@ -76,7 +76,7 @@ struct Shared {
 
 // Largest bin B in [0, nbins) with (keys in bins >= B) >= need, and the
 // number of keys in bins > B.  nbins is 1024 or 2048; the histogram is in LDS.
-static __device__ void find_boundary(const uint32_t* hist, int nbins, int need, int* out_bin,
+static __device__ __forceinline__ void find_boundary(const uint32_t* hist, int nbins, int need, int* out_bin,
                               int* out_above, int* scan_scratch) {
   const int per = nbins / NT;  // bins per thread, taken in descending order
   const int hi = nbins - 1 - threadIdx.x * per;
@@ -103,11 +103,13 @@ static __device__ void find_boundary(const uint32_t* hist, int nbins, int need, 
 // out[0, min(n, m)).  The words are cut into runs of 64; each wave sorts runs
 // in registers (a bitonic network across its lanes), and a word's place is
 // the number of larger words, summed over the runs by a binary search in
-// each.  se[n, 64 * ceil(n / 64)) must hold zero words, which are never larger
+// each, eight runs at a time with no branch (their loads all in flight).
+// se[n, 512 * ceil(n / 512)) must hold zero words, which are never larger
 // than a candidate.
-static __device__ void sort_place(uint64_t* se, int n, int m, uint64_t* out) {
+static __device__ __forceinline__ void sort_place(uint64_t* se, int n, int m, uint64_t* out) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int runs = (n + kRun - 1) / kRun;  // <= kGatherCap / 64 = 34
+  const int runs = (n + kRun - 1) / kRun;         // <= kGatherCap / 64
+  const int runs8 = (runs + 7) / 8 * 8;           // the searches' runs: zero runs past `runs`
   for (int run = wave; run < runs; run += NT / kWave) {
     uint64_t v = se[run * kRun + lane];
     for (int k = 2; k <= kRun; k <<= 1)
@@ -119,19 +121,18 @@ static __device__ void sort_place(uint64_t* se, int n, int m, uint64_t* out) {
     const uint64_t e = se[idx];
     if (e == 0ull) continue;  // padding
     int place = 0;
-    for (int r0 = 0; r0 < runs; r0 += 8) {  // eight runs' searches interleaved
+    for (int r0 = 0; r0 < runs8; r0 += 8) {  // eight runs' searches interleaved
+      const uint64_t* base = se + r0 * kRun;
       int cnt[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) cnt[t] = 0;
 #pragma unroll
       for (int step = kRun / 2; step > 0; step >>= 1) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-          if (r0 + t < runs && se[(r0 + t) * kRun + cnt[t] + step - 1] > e) cnt[t] += step;
+        for (int t = 0; t < 8; ++t) cnt[t] += base[t * kRun + cnt[t] + step - 1] > e ? step : 0;
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        if (r0 + t < runs) place += cnt[t] + (se[(r0 + t) * kRun + cnt[t]] > e ? 1 : 0);
+      for (int t = 0; t < 8; ++t) place += cnt[t] + (base[t * kRun + cnt[t]] > e ? 1 : 0);
     }
     if (place < m) out[place] = e;
   }
@@ -232,7 +233,8 @@ static __device__ void radix_select_words(const Words& src, int c, int m, Shared
   });
   int gathered = above + in_range;  // <= gather_max <= kGatherMax
   gathered = gathered < kGatherMax ? gathered : kGatherMax;
-  if (tid < kRun) sh.se[gathered + tid] = 0ull;
+  const int padded = (gathered + 8 * kRun - 1) / (8 * kRun) * (8 * kRun);  // <= kGatherCap
+  for (int i = gathered + tid; i < padded; i += NT) sh.se[i] = 0ull;
   __syncthreads();
   sort_place(sh.se, gathered, m, sh.se + kGatherCap);
 }
