@@ -37,7 +37,10 @@ Prints one JSON line on stdout.  Besides the contract's keys it carries:
                  kernel's flops against the bf16 MFMA peak (not part of value);
   decode         the 300k x43 and sweep configs decoded serially (each layer's
                  query depends on the previous layer's selection): per-layer
-                 latency of eager launches and of one captured graph replay.
+                 latency of eager launches and of one captured graph replay;
+  pipelined      independent calls of the sweep, 300k x43, 300k and verify
+                 configs in flight on 2 and 3 streams (one handle each): per
+                 call time and the chain's fraction of the HBM peak.
 """
 from __future__ import annotations
 
@@ -91,6 +94,8 @@ def parse():
     ap.add_argument("--no-q8", action="store_true", help="skip the 8-bit key stream leg")
     ap.add_argument("--no-relu", action="store_true", help="skip the per-head ReLU score leg")
     ap.add_argument("--no-decode", action="store_true", help="skip the serial decode legs")
+    ap.add_argument("--no-pipelined", action="store_true",
+                    help="skip the legs with independent calls in flight on several streams")
     ap.add_argument("--calls", type=int, default=200,
                     help="event-bracketed calls per single-call leg")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -563,6 +568,57 @@ def relu_leg(p, stream, steps, warmup):
     }
 
 
+def pipelined_leg(name, engine, calls, streams=(2, 3)):
+    """Independent calls in flight together: S handles on S created streams
+    (default priority), consecutive calls alternating between them, so that one
+    call's latency-bound prep and select overlap another's key stream.  Per
+    call: wall time over `calls` calls between two synchronisations, and the
+    chain's algorithmic bytes over it; parity of the last call's outputs on
+    sampled (layer, row) pairs."""
+    import torch
+    from sparse_attention_block_ds_amd import selector as sel
+    from sparse_attention_block_ds_amd import workloads as wl
+    p = wl.make(name)
+    per_row, ubits = admitted_counts(p)
+    alg = algorithmic_bytes(p, ubits.sum())["total"]
+    n_sets = max(4, math.ceil(COLD_BYTES / alg))
+    sets = [sel.upload(p, "cuda:0") for _ in range(n_sets)]
+    outs = [(torch.empty((p.layers, p.rows, p.k), dtype=torch.int32, device="cuda:0"),
+             torch.empty((p.layers, p.rows, p.k), dtype=torch.float32, device="cuda:0"),
+             torch.empty((p.layers, p.rows), dtype=torch.int32, device="cuda:0")) for _ in range(n_sets)]
+    res = {"workload": WORKLOADS[name], "input_copies": n_sets, "algorithmic_bytes": alg}
+    last = None
+    for S in streams:
+        hs = [sel.Selector(p.layers, p.rows, p.heads, p.dim, p.blocks, p.k, device=0, engine=engine)
+              for _ in range(S)]
+        st = [torch.cuda.Stream() for _ in range(S)]
+
+        def call(i):
+            q, w, keys, mask, limit = sets[i % n_sets]
+            hs[i % S].score_select(q, w, keys, p.k, mask, limit, out=outs[i % n_sets], stream=st[i % S])
+        for i in range(2 * S + 4):
+            call(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(calls):
+            call(i)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / calls
+        last = (calls - 1) % n_sets
+        for h in hs:
+            h.close()
+        res[f"streams_{S}"] = {"us_per_call": us, "chain_frac_hbm": alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                               "candidate_blocks_per_s": float(per_row.sum()) / (us * 1e-6)}
+    out = tuple(t.cpu().numpy() for t in outs[last])
+    pairs = [(l, r) for l in sorted({0, p.layers - 1}) for r in sorted({0, p.rows - 1})]
+    bad = check_parity(p, out, pairs)
+    if bad:
+        log(f"[bench] PARITY FAILURE in the pipelined {name} leg: {bad} pairs")
+        sys.exit(3)
+    res["parity"] = f"{len(pairs)} (layer,row) pairs of the last call vs the oracle"
+    return res
+
+
 def decode_leg(name, stream, reps):
     """Serial decode over the workload's layers (each layer's query depends on
     the previous layer's selection): per-layer device time of eager launches
@@ -776,6 +832,16 @@ def main():
             relu = {"skipped": str(e)}
         torch.cuda.empty_cache()
 
+    pipelined = None
+    if not args.no_pipelined and args.workload == "sweep":
+        pipelined = {}
+        for name, calls in (("sweep", 60), ("300k_x43", 60), ("300k", 400), ("verify", 400)):
+            pipelined[name] = pipelined_leg(name, args.engine, calls)
+            log(f"[bench] pipelined {name}: " + ", ".join(
+                f"{k} {v['us_per_call']:.1f} us/call ({v['chain_frac_hbm']:.3f})"
+                for k, v in pipelined[name].items() if k.startswith("streams_")))
+            torch.cuda.empty_cache()
+
     decode = None
     if not args.no_decode and args.workload == "sweep":
         decode = {}
@@ -833,6 +899,7 @@ def main():
         "q8": q8,
         "relu": relu,
         "decode": decode,
+        "pipelined": pipelined,
     }
     print(json.dumps(line), flush=True)
 
