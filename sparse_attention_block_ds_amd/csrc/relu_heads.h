@@ -32,10 +32,11 @@ __device__ __forceinline__ int relu_w_offset_words(int rows, int hp) {
   return (rows * hp * (D + 8) * 2 + 15) / 16 * 4;  // 16-byte aligned, in 32-bit words
 }
 
-// Cooperative copy of layer l's query heads and weights into the stage (all
-// threads of the workgroup call it; the caller synchronises afterwards).
+// Cooperative copy of the query heads and weights of R consecutive rows, from
+// (layer, row) index lr0 on, into the stage (all threads of the workgroup call
+// it; the caller synchronises afterwards).
 template <int R, int D>
-__device__ __forceinline__ ReluStage relu_stage_heads(const Call& c, int l, uint32_t* lds, int tid,
+__device__ __forceinline__ ReluStage relu_stage_heads(const Call& c, int64_t lr0, uint32_t* lds, int tid,
                                                       int nthreads) {
   const int H = c.heads, hp = (H + 15) / 16 * 16;
   constexpr int QS = D + 8;
@@ -46,12 +47,12 @@ __device__ __forceinline__ ReluStage relu_stage_heads(const Call& c, int l, uint
     const int c8 = x % (D / 8), rh = x / (D / 8);
     const int r = rh / hp, h = rh % hp;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (h < H) v = *reinterpret_cast<const uint4*>(c.q + (((int64_t)l * R + r) * H + h) * D + 8 * c8);
+    if (h < H) v = *reinterpret_cast<const uint4*>(c.q + ((lr0 + r) * H + h) * D + 8 * c8);
     *reinterpret_cast<uint4*>(qs + (int64_t)rh * QS + 8 * c8) = v;
   }
   for (int x = tid; x < R * hp; x += nthreads) {
     const int r = x / hp, h = x % hp;
-    ws[x] = h < H ? bf16_to_f32(c.w[((int64_t)l * R + r) * H + h]) : 0.0f;
+    ws[x] = h < H ? bf16_to_f32(c.w[(lr0 + r) * H + h]) : 0.0f;
   }
   return ReluStage{qs, ws, hp};
 }

@@ -381,7 +381,7 @@ struct ReluEngine {
   ReluStage st;
 
   __device__ void init(const Call& c, int l, uint32_t* lds) {
-    st = relu_stage_heads<R, D>(c, l, lds, threadIdx.x, kScoreThreads);
+    st = relu_stage_heads<R, D>(c, (int64_t)l * R, lds, threadIdx.x, kScoreThreads);
   }
 
   // Groups ga and gb (both valid group starts) into buffer B.
