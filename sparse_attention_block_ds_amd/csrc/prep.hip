@@ -540,58 +540,87 @@ __device__ void row_tile(const Call& c, int l, int r, typename Sampler::Shared& 
   }
 }
 
-// Workgroup x >= 1 of layer l: expand tiles [16 (x-1), 16 x) of the union.
+// Expanding workgroups per layer: one per 16 tiles, at most kMaxExpanders.
+// Expander x (1-based) takes the contiguous tiles [(x-1) tpe, x tpe), tpe
+// the tiles per expander rounded up to a multiple of 16, in rounds of 16 (one
+// tile per wave).  Each expander counts the admitted blocks of every tile
+// before its own, so each mask word is read at most kMaxExpanders times and
+// the work stays linear in N.
+constexpr int kMaxExpanders = 64;
+__host__ __device__ __forceinline__ int prep_expanders(int ntiles) {
+  const int e = (ntiles + kPrepTilesPerWg - 1) / kPrepTilesPerWg;
+  return e < kMaxExpanders ? e : kMaxExpanders;
+}
+__host__ __device__ __forceinline__ int expander_tiles(int ntiles, int expanders) {
+  const int per = (ntiles + expanders - 1) / expanders;
+  return (per + kPrepTilesPerWg - 1) / kPrepTilesPerWg * kPrepTilesPerWg;
+}
+
+// Expanding workgroup x >= 1 of layer l: its tiles of the union, in order.
 template <int R>
 __device__ void expand_tiles(const Call& c, int l, int x, ExpandShared& sh) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int tpe = expander_tiles(c.ntiles, prep_expanders(c.ntiles));
+  const int t_begin = (x - 1) * tpe;
+  if (t_begin >= c.ntiles) return;  // uniform: nothing left for this expander
+  const int t_end = t_begin + tpe < c.ntiles ? t_begin + tpe : c.ntiles;
   const Limits s = layer_limits<R>(c, l);
   const uint32_t* mask_l = c.mask + (int64_t)l * c.mask_layer_stride;
   const int64_t words = (s.maxlim + 31) / 32;
-  const int t0 = (x - 1) * kPrepTilesPerWg;
 
-  // this wave's tile word (loaded alongside the earlier tiles' words)
-  const int t = t0 + wave;
-  const int64_t j = (int64_t)t * kTileWords + lane;
-  const uint32_t u = (t < c.ntiles && j < words) ? union_word<R>(c, mask_l, s, j) : 0u;
+  // the first round's tile word (loaded alongside the earlier tiles' words)
+  int t = t_begin + wave;
+  int64_t j = (int64_t)t * kTileWords + lane;
+  uint32_t u = (t < t_end && j < words) ? union_word<R>(c, mask_l, s, j) : 0u;
 
   // admitted blocks of all earlier tiles
   int before = 0;
-  const int64_t w_end = (int64_t)t0 * kTileWords < words ? (int64_t)t0 * kTileWords : words;
+  const int64_t w_end = (int64_t)t_begin * kTileWords < words ? (int64_t)t_begin * kTileWords : words;
   for (int64_t jj = tid; jj < w_end; jj += kPrepThreads) before += __popc(union_word<R>(c, mask_l, s, jj));
   if (tid == 0) sh.before = 0;
   __syncthreads();
   before = wave_sum(before);
   if (lane == 0 && before) atomicAdd(&sh.before, before);
 
-  // place the tile's admitted blocks in order: lane i's k-th set bit goes to
-  // its exclusive prefix + k.  Each lane walks its 32 bits starting at bit
-  // i % 32, so at every step the lanes write to different LDS banks.
-  const int cnt = __popc(u);
-  const int in_tile = wave_inclusive_scan(cnt) - cnt;
-  const int tile_total = __shfl(in_tile + cnt, kWave - 1, kWave);
-  if (lane == 0) sh.tile_cnt[wave] = tile_total;
-  const int32_t b0 = (int32_t)(j * 32);
-  const int32_t tb = t * kTileBlocks;  // the tile's first block
-  for (int step = 0; step < 32; ++step) {
-    const int bit = (step + lane) & 31;
-    if ((u >> bit) & 1u) sh.stage[wave][in_tile + __popc(u & ((1u << bit) - 1u))] = (uint16_t)(b0 + bit - tb);
+  for (int t0 = t_begin; t0 < t_end; t0 += kPrepTilesPerWg) {
+    if (t0 != t_begin) {
+      t = t0 + wave;
+      j = (int64_t)t * kTileWords + lane;
+      u = (t < t_end && j < words) ? union_word<R>(c, mask_l, s, j) : 0u;
+    }
+    // place the tile's admitted blocks in order: lane i's k-th set bit goes to
+    // its exclusive prefix + k.  Each lane walks its 32 bits starting at bit
+    // i % 32, so at every step the lanes write to different LDS banks.
+    const int cnt = __popc(u);
+    const int in_tile = wave_inclusive_scan(cnt) - cnt;
+    const int tile_total = __shfl(in_tile + cnt, kWave - 1, kWave);
+    if (lane == 0) sh.tile_cnt[wave] = tile_total;
+    const int32_t b0 = (int32_t)(j * 32);
+    const int32_t tb = t * kTileBlocks;  // the tile's first block
+#pragma unroll 1  // unrolled, the 32 placements need more than 128 VGPRs
+    for (int step = 0; step < 32; ++step) {
+      const int bit = (step + lane) & 31;
+      if ((u >> bit) & 1u) sh.stage[wave][in_tile + __popc(u & ((1u << bit) - 1u))] = (uint16_t)(b0 + bit - tb);
+    }
+    __syncthreads();
+    int total = 0;
+    const int mine = tid < kPrepWaves ? sh.tile_cnt[tid] : 0;
+    const int excl = block_exclusive_scan<kPrepThreads>(mine, &total, sh.scan);
+    if (tid < kPrepWaves) sh.tile_cnt[tid] = excl;
+    __syncthreads();
+    int32_t* out = c.list + (int64_t)l * c.blocks + sh.before + sh.tile_cnt[wave];
+    for (int i = lane; i < tile_total; i += kWave) out[i] = tb + (int32_t)sh.stage[wave][i];
+    __syncthreads();  // the round's counts and runs are read before the next round rewrites them
+    if (tid == 0) sh.before += total;
   }
-  __syncthreads();
-  int total = 0;
-  const int mine = tid < kPrepWaves ? sh.tile_cnt[tid] : 0;
-  const int excl = block_exclusive_scan<kPrepThreads>(mine, &total, sh.scan);
-  if (tid < kPrepWaves) sh.tile_cnt[tid] = excl;
-  __syncthreads();
-  int32_t* out = c.list + (int64_t)l * c.blocks + sh.before + sh.tile_cnt[wave];
-  for (int i = lane; i < tile_total; i += kWave) out[i] = tb + (int32_t)sh.stage[wave][i];
 }
 
-template <int R, int D, class Sampler>
 // At most 80 SGPRs: measured on gfx950, a 1024-thread workgroup whose waves
 // hold 96 or more SGPRs leaves no room for a second one on its compute unit
 // (and a few SGPRs then spill into VGPR lanes instead), while at 80 two row
 // or expanding workgroups share a unit, which the layers' R + E workgroups
 // per layer need once they outnumber the units.
+template <int R, int D, class Sampler>
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_num_sgpr(80))) void prep_kernel(Call c) {
   __shared__ PrepShared<typename Sampler::Shared> sh;
   // blockIdx.x is the layer, so that consecutive workgroups (which the
@@ -626,7 +655,7 @@ hipError_t launch_r(const Call& c, dim3 grid, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prep(const Call& c, hipStream_t stream) {
-  const int expanders = c.mode == kNoMask ? 0 : (c.ntiles + kPrepTilesPerWg - 1) / kPrepTilesPerWg;
+  const int expanders = c.mode == kNoMask ? 0 : prep_expanders(c.ntiles);
   dim3 grid(c.layers, c.rows + expanders);
   switch (c.rows) {
     case 1: return launch_r<1>(c, grid, stream);

@@ -251,3 +251,22 @@ def test_capacity_error_leaves_outputs_untouched(selector):
     assert e.value.status == sel.DS_SEL_E_CAPACITY
     torch.cuda.synchronize()
     assert all(bool((t == 7).all()) for t in out)
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_many_tiles_expander_rounds(shared):
+    """2.3 M blocks are 1,124 tiles of 2,048: more than 64 expanding workgroups'
+    worth, so each of the 64 takes 32 tiles in two rounds of 16 (and the last
+    ones have none).  Bit-exact on integer inputs, shared and per-row masks."""
+    import torch
+    p = wl.make_custom(1, 2, 4, 32, 2_300_000, 64, seed=330 + int(shared), values="int3", mask_p=0.5,
+                       mask_shared=shared, limits=np.array([[2_300_000, 1_700_003]], np.int32))
+    _print_case(f"many_tiles shared={shared}", p)
+    s = sel.Selector(max_layers=1, max_rows=2, max_heads=4, max_dim=32, max_blocks=p.blocks, max_k=64,
+                     device=0)
+    try:
+        got = gs.run_gpu(s, p)
+        torch.cuda.synchronize()
+    finally:
+        s.close()
+    gs.assert_bit_exact(got, gs.run_oracle(p), f"many_tiles shared={shared}")
