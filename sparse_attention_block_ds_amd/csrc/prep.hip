@@ -261,9 +261,13 @@ struct SampleMfmaQ8 {
 
   __device__ void stage(const Call&, int64_t, Shared&) {}
 
+  // One 32-column group at a time over both sample groups, so that each
+  // group's A operand, codes and scales are dead once its MFMAs are issued.
   __device__ void finish(int64_t n, int S, int64_t lim, Shared& sh) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-    bf16x8_t a[KC];
+    float sc[kGroupsPerWave];
+#pragma unroll
+    for (int g = 0; g < kGroupsPerWave; ++g) sc[g] = 0.f;
 #pragma unroll
     for (int cc = 0; cc < KC; ++cc) {
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -273,23 +277,22 @@ struct SampleMfmaQ8 {
         for (int e = 0; e < 4; ++e)
           v[e] = (uint32_t)f32_to_bf16_rne(qr[2 * e]) | ((uint32_t)f32_to_bf16_rne(qr[2 * e + 1]) << 16);
       }
-      a[cc] = __builtin_bit_cast(bf16x8_t, v);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, v);
+#pragma unroll
+      for (int g = 0; g < kGroupsPerWave; ++g) {
+        const u32x4_t bv = {bf16_pair_of_codes(kb[g][cc].x, 0), bf16_pair_of_codes(kb[g][cc].x, 16),
+                            bf16_pair_of_codes(kb[g][cc].y, 0), bf16_pair_of_codes(kb[g][cc].y, 16)};
+        const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, __builtin_bit_cast(bf16x8_t, bv), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        sc[g] += half_bits_to_f32(ks[g][cc]) * acc[0];
+      }
     }
 #pragma unroll
     for (int g = 0; g < kGroupsPerWave; ++g) {
       const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
-      float sc = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < KC; ++cc) {
-        const u32x4_t bv = {bf16_pair_of_codes(kb[g][cc].x, 0), bf16_pair_of_codes(kb[g][cc].x, 16),
-                            bf16_pair_of_codes(kb[g][cc].y, 0), bf16_pair_of_codes(kb[g][cc].y, 16)};
-        const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            a[cc], __builtin_bit_cast(bf16x8_t, bv), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        sc += half_bits_to_f32(ks[g][cc]) * acc[0];
-      }
       if (lane < 16 && j < S) {
         const int64_t b = sample_block(j, n);
-        if (b < lim && ((mw[g] >> (b & 31)) & 1u)) sh.skey[j] = score_to_key(sc);
+        if (b < lim && ((mw[g] >> (b & 31)) & 1u)) sh.skey[j] = score_to_key(sc[g]);
       }
     }
   }
