@@ -78,15 +78,15 @@ struct Shared {
 // number of keys in bins > B.  nbins is 1024 or 2048; the histogram is in LDS.
 static __device__ __forceinline__ void find_boundary(const uint32_t* hist, int nbins, int need, int* out_bin,
                               int* out_above, int* scan_scratch) {
-  const int per = nbins / NT;  // bins per thread, taken in descending order
-  const int hi = nbins - 1 - threadIdx.x * per;
+  const int per = (nbins + NT - 1) / NT;  // bins per thread, taken in descending order
+  const int hi = nbins - 1 - threadIdx.x * per;  // the last threads may hold fewer (or no) bins
   int mine = 0;
-  for (int i = 0; i < per; ++i) mine += (int)hist[hi - i];
+  for (int i = 0; i < per && hi - i >= 0; ++i) mine += (int)hist[hi - i];
   int total = 0;
   const int excl = block_exclusive_scan<NT>(mine, &total, scan_scratch);
   if (excl < need && excl + mine >= need) {
     int above = excl;
-    for (int i = 0; i < per; ++i) {
+    for (int i = 0; i < per && hi - i >= 0; ++i) {
       const int cnt = (int)hist[hi - i];
       if (above + cnt >= need) {
         *out_bin = hi - i;
@@ -144,7 +144,7 @@ static __device__ __forceinline__ void sort_place(uint64_t* se, int n, int m, ui
 // lies inside the row's list (which has room for every position), and the
 // slots at or past c are simply never used.
 struct RegisterWords {
-  static constexpr int kPer = kSelectBuf / NT;
+  static constexpr int kPer = (kSelectBuf + NT - 1) / NT;
   uint64_t v[kPer];
   int c = 0;
   // The first half of the slots, before the count is known (the usual lists
@@ -383,14 +383,15 @@ __global__ __launch_bounds__(NT) void select_kernel(Call c) {
 
 hipError_t launch_select(const Call& c, hipStream_t stream) {
   // One workgroup per (layer, row).  A 1,024-thread workgroup is fastest for a
-  // row, but only one is resident per compute unit; when the rows outnumber
-  // the compute units, 512-thread workgroups (two per unit) keep every row in
-  // one round.
+  // row, but only one is resident per compute unit (its waves hold more than
+  // 80 SGPRs); when the rows outnumber the compute units, 768-thread
+  // workgroups (three waves per SIMD, two per unit) keep every row in one
+  // round.
   const int64_t rows = (int64_t)c.layers * c.rows;
   const int64_t cus = c.score_slots / kScoreWgsPerCu;
   dim3 grid(c.rows, c.layers);
   if (rows > cus)
-    hipLaunchKernelGGL(select_kernel<512>, grid, dim3(512), 0, stream, c);
+    hipLaunchKernelGGL(select_kernel<768>, grid, dim3(768), 0, stream, c);
   else
     hipLaunchKernelGGL(select_kernel<1024>, grid, dim3(1024), 0, stream, c);
   return hipGetLastError();

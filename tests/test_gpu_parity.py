@@ -200,6 +200,32 @@ def test_more_rows_than_compute_units(selector, k):
     gs.assert_bit_exact(gpu, gs.run_oracle(p), f"many_rows_k{k}")
 
 
+def test_more_rows_than_compute_units_every_select_path(selector):
+    """43 x 8 selections with the smaller select workgroups, through the select's
+    slow paths: on even layers half of the 20000 blocks tie at the top, so more
+    candidates pass the floor than the registers hold; on odd layers the sampled
+    blocks hold the top scores, so the floor passes fewer than k and every row
+    is rescored."""
+    rng = np.random.default_rng(11)
+    L, R, H, d, N, k = 43, 8, 1, 64, 20000, 512
+    q = np.zeros((L, R, H, d), np.float32)
+    q[:, :, 0, 0] = 1.0
+    w = np.ones((L, R, H), np.float32)
+    keys = np.zeros((L, N, d), np.float32)
+    sampled = (2 * np.arange(512) + 1) * N // 1024
+    for l in range(L):
+        if l % 2 == 0:
+            keys[l, :, 0] = 1.0 + rng.integers(0, 2, N) / 2.0
+        else:
+            col0 = 1.0 + rng.integers(0, 128, N) / 128.0
+            col0[sampled] = 2.0 + rng.integers(0, 128, 512) / 64.0
+            keys[l, :, 0] = col0
+    p = wl.Problem("many_rows_paths", k, wl.f32_to_bf16_bits(q), wl.f32_to_bf16_bits(w),
+                   wl.f32_to_bf16_bits(keys), None, None, True)
+    _print_case("many_rows_paths", p)
+    gs.assert_bit_exact(gs.run_gpu(selector, p), gs.run_oracle(p), "many_rows_paths")
+
+
 def test_repeated_calls_identical(selector):
     """Atomic append order must not leak into the output (tie-heavy input)."""
     import torch
