@@ -30,7 +30,8 @@ constexpr int kSampleSlots = 512;                   // blocks per layer scored t
 
 constexpr int kScoreThreads = 256;           // 4 waves
 constexpr int kScorePieceMax = 2048;         // admitted positions per score workgroup: at most,
-constexpr int kScorePieceMin = 64;           // and at least
+constexpr int kScorePieceMin = 256;          // and at least: on small calls fewer, longer pieces
+                                             // finish sooner than one short piece per slot
 constexpr int kScoreWgsPerCu = 4;            // resident score workgroups per compute unit
 constexpr int kWaveStage = 512;              // per-wave candidate staging, all rows (LDS)
 constexpr int kCountPad = 32;                // candidate counters sit 128 bytes apart

@@ -584,7 +584,7 @@ __device__ __forceinline__ void stream_piece_pairs(Engine& eng, PieceCtx<Engine:
 
 // Which piece this workgroup streams.  Every layer's admitted positions are
 // cut into pieces of T positions, where T = ceil(total / (slots - L)) clamped
-// to [64, 2048], total is the admitted count summed over layers and slots the
+// to [256, 2048], total is the admitted count summed over layers and slots the
 // resident workgroups of the device; the layers' pieces are numbered in layer
 // order and workgroup j takes piece j.  There are at most total / T + L pieces:
 // no more than the slots unless T had to be clamped to 2048, and never more
