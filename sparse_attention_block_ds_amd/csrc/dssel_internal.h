@@ -26,7 +26,7 @@ constexpr int kTileWords = kTileBlocks / 32;
 
 constexpr int kPrepThreads = 1024;                  // 16 waves
 constexpr int kPrepTilesPerWg = kPrepThreads / 64;  // tiles expanded per prep workgroup
-constexpr int kSampleSlots = 512;                   // blocks per layer scored to place the floors
+constexpr int kSampleSlots = 512;                   // the most blocks per row scored to place the floor
 
 constexpr int kScoreThreads = 256;           // 4 waves
 constexpr int kScorePieceMax = 2048;         // admitted positions per score workgroup: at most,

@@ -29,15 +29,16 @@
 //
 // Candidate floors (the same row workgroups): the key stream writes only keys
 // that can still be among a row's best k, i.e. keys at or above the row's
-// floor.  The floor comes from 512 blocks spread evenly over [0, N), scored on
-// the matrix cores: per row, the floor is the sampled key of rank about three
-// times more selective than k would suggest (3 k n_sample / n_admitted, plus
-// 8), found by a bitwise search over the wave's ballots.  Any floor is safe:
+// floor.  The floor comes from 512 blocks (256 on a one-layer call) spread
+// evenly over [0, N), scored on the matrix cores: per row, the floor is the
+// sampled key of rank about three times more selective than k would suggest
+// (3 k n_sample / n_admitted, plus 8), found by a bitwise search over the
+// wave's ballots.  Any floor is safe:
 // the candidate lists have room for every position, and the select rescores the
 // row exactly when fewer than min(k, admitted) candidates came through. The
-// floor only decides how few keys are written; at 512 samples and 75000
-// admitted blocks the expected sample count above the k-th key is 3.5 and the
-// rank taken is 19, so a rescore is a ~1e-8 event.
+// floor only decides how few keys are written; at 75000 admitted blocks the
+// expected sample count above the k-th key is 3.5 with 512 samples (rank taken
+// 19) and 1.75 with 256 (rank 14), so a rescore is a ~1e-8 event either way.
 #include "device_util.h"
 #include "dssel_internal.h"
 #include "relu_heads.h"
@@ -132,42 +133,53 @@ union PrepShared {
   ExpandShared e;
 };
 
-// Block of sample slot j: (2 j + 1) * N / (2 S) with S = min(512, N), i.e. the
-// middle of the j-th of S equal stretches of [0, N).
+// Block of sample slot j of NS: (2 j + 1) * N / (2 NS) when N >= NS, i.e. the
+// middle of the j-th of NS equal stretches of [0, N), else block j.
+template <int NS>
 __device__ __forceinline__ int64_t sample_block(int j, int64_t n) {
-  return n >= kSampleSlots ? ((2 * (int64_t)j + 1) * n) >> 10 : j;
+  constexpr int kShift = __builtin_ctz(2 * NS);
+  static_assert((1 << kShift) == 2 * NS, "sample_block divides by 2 NS with a shift");
+  return n >= NS ? ((2 * (int64_t)j + 1) * n) >> kShift : j;
 }
-static_assert(kSampleSlots == 512, "sample_block divides by 2 * 512 with a shift");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kSampleGroups = kSampleSlots / 16;                // 16 sampled blocks per MFMA
-constexpr int kGroupsPerWave = kSampleGroups / (kPrepThreads / kWave);  // 2
+// Sampled blocks per row: 512 on batched calls, where a tighter floor saves
+// the key stream and the select more than the samples cost; 256 on one-layer
+// calls, where the row workgroup's sample loads are on the critical path
+// (measured on gfx950: prep 2.7 us shorter, the whole call 1.7-2.7 us).
+constexpr int kSamplesBatched = kSampleSlots;  // 512: the LDS holds this many keys
+constexpr int kSamplesOneLayer = 256;
+// Groups of 16 sampled blocks (one MFMA each) per wave.
+template <int NS>
+constexpr int kGroupsPerWave = NS / 16 / (kPrepThreads / kWave);
 
 // Sampled keys of one row on the matrix cores.  A floor only has to be a
 // reasonable guess (any floor is exact, see above), so the sampled scores use
 // q~ rounded to bf16: one v_mfma_f32_16x16x32_bf16 per 32 columns gives 16
 // sampled blocks (B columns, block = lane % 16) against the row (A row 0, the
 // other 15 A rows zero); lanes 0-15 then hold the row's 16 scores.  Each wave
-// takes groups wave and wave + 16 of 16 slots.  Loads are unconditional when
+// takes groups wave, wave + 16, ... of 16 slots (G of them).  Loads are unconditional when
 // there are blocks (slots past S re-read slot 0 and are not admitted), so no
 // branch waits on them; nothing is read when there are none (S = 0).
-template <int D>
+template <int D, int NS>
 struct SampleMfma {
+  static constexpr int kSamples = NS;
+  static constexpr int G = kGroupsPerWave<NS>;
   static constexpr bool kFold = true;  // scores on the folded query
   using Shared = FoldShared<0>;
   static constexpr int KC = D / 32;
-  u32x4_t kb[kGroupsPerWave][KC];
-  uint32_t mw[kGroupsPerWave];  // the row's mask word at the lane's block
+  u32x4_t kb[G][KC];
+  uint32_t mw[G];  // the row's mask word at the lane's block
 
   // mrow: the row's mask words, or null when there is no mask.
   __device__ void issue(const Call& c, int l, int64_t n, const uint32_t* mrow, int S) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const uint16_t* K = c.keys + (int64_t)l * c.key_layer_stride;
 #pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) {
+    for (int g = 0; g < G; ++g) {
       const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
       if (S == 0) {
 #pragma unroll
@@ -175,7 +187,7 @@ struct SampleMfma {
         mw[g] = 0u;
         continue;
       }
-      const int64_t b = sample_block(j < S ? j : 0, n);
+      const int64_t b = sample_block<NS>(j < S ? j : 0, n);
       const uint16_t* row = K + b * c.ldk + 8 * (lane >> 4);
 #pragma unroll
       for (int cc = 0; cc < KC; ++cc) kb[g][cc] = *reinterpret_cast<const u32x4_t*>(row + 32 * cc);
@@ -190,9 +202,9 @@ struct SampleMfma {
   // operand and B operands are dead once its MFMAs are issued.
   __device__ void finish(int64_t n, int S, int64_t lim, Shared& sh) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-    f32x4_t acc[kGroupsPerWave];
+    f32x4_t acc[G];
 #pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < G; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < KC; ++cc) {
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -204,15 +216,15 @@ struct SampleMfma {
       }
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, v);
 #pragma unroll
-      for (int g = 0; g < kGroupsPerWave; ++g)
+      for (int g = 0; g < G; ++g)
         acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, kb[g][cc]), acc[g],
                                                          0, 0, 0);
     }
 #pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) {
+    for (int g = 0; g < G; ++g) {
       const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
       if (lane < 16 && j < S) {
-        const int64_t b = sample_block(j, n);
+        const int64_t b = sample_block<NS>(j, n);
         if (b < lim && ((mw[g] >> (b & 31)) & 1u)) sh.skey[j] = score_to_key(acc[g][0]);
       }
     }
@@ -222,21 +234,23 @@ struct SampleMfma {
 // The same sampled scores on 8-bit keys: each 32-column group is one MFMA
 // with its own accumulation (codes widened exactly to bf16), scaled by the
 // block's group scale and summed in fp32.
-template <int D>
+template <int D, int NS>
 struct SampleMfmaQ8 {
+  static constexpr int kSamples = NS;
+  static constexpr int G = kGroupsPerWave<NS>;
   static constexpr bool kFold = true;
   using Shared = FoldShared<0>;
   static constexpr int KC = D / 32;
-  uint2 kb[kGroupsPerWave][KC];
-  uint16_t ks[kGroupsPerWave][KC];
-  uint32_t mw[kGroupsPerWave];
+  uint2 kb[G][KC];
+  uint16_t ks[G][KC];
+  uint32_t mw[G];
 
   __device__ void issue(const Call& c, int l, int64_t n, const uint32_t* mrow, int S) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int8_t* codes = c.codes + (int64_t)l * c.code_layer_stride;
     const uint16_t* scales = c.scales + (int64_t)l * c.scale_layer_stride;
 #pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) {
+    for (int g = 0; g < G; ++g) {
       const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
       if (S == 0) {
 #pragma unroll
@@ -247,7 +261,7 @@ struct SampleMfmaQ8 {
         mw[g] = 0u;
         continue;
       }
-      const int64_t b = sample_block(j < S ? j : 0, n);
+      const int64_t b = sample_block<NS>(j < S ? j : 0, n);
       const int8_t* row = codes + b * c.ldc + 8 * (lane >> 4);
 #pragma unroll
       for (int cc = 0; cc < KC; ++cc) {
@@ -265,9 +279,9 @@ struct SampleMfmaQ8 {
   // group's A operand, codes and scales are dead once its MFMAs are issued.
   __device__ void finish(int64_t n, int S, int64_t lim, Shared& sh) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-    float sc[kGroupsPerWave];
+    float sc[G];
 #pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) sc[g] = 0.f;
+    for (int g = 0; g < G; ++g) sc[g] = 0.f;
 #pragma unroll
     for (int cc = 0; cc < KC; ++cc) {
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -279,7 +293,7 @@ struct SampleMfmaQ8 {
       }
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, v);
 #pragma unroll
-      for (int g = 0; g < kGroupsPerWave; ++g) {
+      for (int g = 0; g < G; ++g) {
         const u32x4_t bv = {bf16_pair_of_codes(kb[g][cc].x, 0), bf16_pair_of_codes(kb[g][cc].x, 16),
                             bf16_pair_of_codes(kb[g][cc].y, 0), bf16_pair_of_codes(kb[g][cc].y, 16)};
         const f32x4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -288,10 +302,10 @@ struct SampleMfmaQ8 {
       }
     }
 #pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) {
+    for (int g = 0; g < G; ++g) {
       const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
       if (lane < 16 && j < S) {
-        const int64_t b = sample_block(j, n);
+        const int64_t b = sample_block<NS>(j, n);
         if (b < lim && ((mw[g] >> (b & 31)) & 1u)) sh.skey[j] = score_to_key(sc[g]);
       }
     }
@@ -302,20 +316,22 @@ struct SampleMfmaQ8 {
 // blocks and mask words as SampleMfma, scored against every head of the row
 // on the matrix cores (relu_heads.h) with the row's heads staged in LDS; no
 // fold.
-template <int D>
+template <int D, int NS>
 struct SampleRelu {
+  static constexpr int kSamples = NS;
+  static constexpr int G = kGroupsPerWave<NS>;
   static constexpr bool kFold = false;
   using Shared = FoldShared<kReluStageBytes / 4>;
   static constexpr int KC = D / 32;
-  relu_u32x4_t kb[kGroupsPerWave][KC];
-  uint32_t mw[kGroupsPerWave];
+  relu_u32x4_t kb[G][KC];
+  uint32_t mw[G];
   ReluStage st;
 
   __device__ void issue(const Call& c, int l, int64_t n, const uint32_t* mrow, int S) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const uint16_t* K = c.keys + (int64_t)l * c.key_layer_stride;
 #pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) {
+    for (int g = 0; g < G; ++g) {
       const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
       if (S == 0) {
 #pragma unroll
@@ -323,7 +339,7 @@ struct SampleRelu {
         mw[g] = 0u;
         continue;
       }
-      const int64_t b = sample_block(j < S ? j : 0, n);
+      const int64_t b = sample_block<NS>(j < S ? j : 0, n);
       const uint16_t* row = K + b * c.ldk + 8 * (lane >> 4);
 #pragma unroll
       for (int cc = 0; cc < KC; ++cc) kb[g][cc] = *reinterpret_cast<const relu_u32x4_t*>(row + 32 * cc);
@@ -341,31 +357,32 @@ struct SampleRelu {
   __device__ void finish(int64_t n, int S, int64_t lim, Shared& sh) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
 #pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) {
+    for (int g = 0; g < G; ++g) {
       float one[1][1];
       relu_all_rows<1, D, 1, false>(st, reinterpret_cast<const relu_u32x4_t(&)[1][KC]>(kb[g]), one);
       const int j = (wave + g * (kPrepThreads / kWave)) * 16 + (lane & 15);
       if (lane < 16 && j < S) {
-        const int64_t b = sample_block(j, n);
+        const int64_t b = sample_block<NS>(j, n);
         if (b < lim && ((mw[g] >> (b & 31)) & 1u)) sh.skey[j] = score_to_key(one[0][0]);
       }
     }
   }
 };
 
-// A floor for the j-th largest of the 512 keys a wave holds (8 per lane): the
-// largest x with at least j keys >= x, built bit by bit from the top, over
+// A floor for the j-th largest of the NS keys a wave holds (NS / 64 per lane):
+// the largest x with at least j keys >= x, built bit by bit from the top, over
 // the top 16 bits only (sign, exponent and 7 mantissa bits of the score).
 // It is at most the j-th largest key and lets through at most the keys that
 // share its 16-bit prefix besides.
-__device__ __forceinline__ uint32_t wave_jth_largest(const uint32_t (&v)[kSampleSlots / kWave], int j) {
+template <int NS>
+__device__ __forceinline__ uint32_t wave_jth_largest(const uint32_t (&v)[NS / kWave], int j) {
   uint32_t x = 0;
 #pragma unroll 1
   for (int bit = 31; bit >= 16; --bit) {
     const uint32_t t = x | (1u << bit);
     int n = 0;
 #pragma unroll
-    for (int i = 0; i < kSampleSlots / kWave; ++i) n += __popcll(__ballot(v[i] >= t));
+    for (int i = 0; i < NS / kWave; ++i) n += __popcll(__ballot(v[i] >= t));
     if (n >= j) x = t;
   }
   return x;
@@ -382,7 +399,7 @@ __device__ __forceinline__ int64_t row_limit(const Call& c, int l, int r) {
 // mask words at them are issued first, then the row's query heads and
 // weights, then the mask words to count.  One workgroup per row keeps the
 // bytes each compute unit pulls in small: the row's heads (H d bf16) and the
-// 512 sampled key rows.
+// sampled key rows.
 template <int R, int D, class Sampler>
 __device__ void row_tile(const Call& c, int l, int r, typename Sampler::Shared& sh) {
   const int H = c.heads;
@@ -396,10 +413,10 @@ __device__ void row_tile(const Call& c, int l, int r, typename Sampler::Shared& 
   // Sampled key rows: spread over [0, N), so that their addresses wait for
   // nothing (samples at or past the row's limit are simply not admitted).
   const int64_t N = c.blocks;
-  const int S = N < kSampleSlots ? (int)N : kSampleSlots;
+  const int S = N < Sampler::kSamples ? (int)N : Sampler::kSamples;
   Sampler smp;
   smp.issue(c, l, N, mrow, S);
-  for (int i = tid; i < kSampleSlots; i += kPrepThreads) sh.skey[i] = 0u;
+  for (int i = tid; i < Sampler::kSamples; i += kPrepThreads) sh.skey[i] = 0u;
 
   // fold, first half: thread (slice hs, chunk) sums w_h q_h[i0 .. i0 + 4) over
   // its slice of heads, ascending h, four heads' loads at a time.  Four
@@ -522,10 +539,11 @@ __device__ void row_tile(const Call& c, int l, int r, typename Sampler::Shared& 
 
   // floor: wave 0 finds the row's jth largest sample key
   if (tid < kWave) {
-    uint32_t v[kSampleSlots / kWave];
+    constexpr int NS = Sampler::kSamples;
+    uint32_t v[NS / kWave];
     int sr = 0;  // admitted samples: the non-zero keys
 #pragma unroll
-    for (int i = 0; i < kSampleSlots / kWave; ++i) {
+    for (int i = 0; i < NS / kWave; ++i) {
       v[i] = sh.skey[i * kWave + lane];
       sr += __popcll(__ballot(v[i] != 0u));
     }
@@ -534,7 +552,7 @@ __device__ void row_tile(const Call& c, int l, int r, typename Sampler::Shared& 
     uint32_t floor = 0;
     if (sr > 0 && n > 3 * m) {
       const int64_t jth = (3 * m * sr + n - 1) / n + 8;
-      if (jth <= sr) floor = wave_jth_largest(v, (int)jth);
+      if (jth <= sr) floor = wave_jth_largest<NS>(v, (int)jth);
     }
     if (lane == 0) {
       c.floor_key[lr] = floor;
@@ -633,14 +651,20 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_num_sgpr(80))) 
   else expand_tiles<R>(c, blockIdx.x, blockIdx.y - R + 1, sh.e);
 }
 
+template <int R, int D, int NS>
+void launch_rdn(const Call& c, dim3 grid, hipStream_t stream) {
+  if (c.fmt == kKeysQ8)
+    hipLaunchKernelGGL((prep_kernel<R, D, SampleMfmaQ8<D, NS>>), grid, dim3(kPrepThreads), 0, stream, c);
+  else if (c.score_kind == kScoreHeadRelu)
+    hipLaunchKernelGGL((prep_kernel<R, D, SampleRelu<D, NS>>), grid, dim3(kPrepThreads), 0, stream, c);
+  else
+    hipLaunchKernelGGL((prep_kernel<R, D, SampleMfma<D, NS>>), grid, dim3(kPrepThreads), 0, stream, c);
+}
+
 template <int R, int D>
 void launch_rd(const Call& c, dim3 grid, hipStream_t stream) {
-  if (c.fmt == kKeysQ8)
-    hipLaunchKernelGGL((prep_kernel<R, D, SampleMfmaQ8<D>>), grid, dim3(kPrepThreads), 0, stream, c);
-  else if (c.score_kind == kScoreHeadRelu)
-    hipLaunchKernelGGL((prep_kernel<R, D, SampleRelu<D>>), grid, dim3(kPrepThreads), 0, stream, c);
-  else
-    hipLaunchKernelGGL((prep_kernel<R, D, SampleMfma<D>>), grid, dim3(kPrepThreads), 0, stream, c);
+  if (c.layers == 1) launch_rdn<R, D, kSamplesOneLayer>(c, grid, stream);
+  else launch_rdn<R, D, kSamplesBatched>(c, grid, stream);
 }
 
 template <int R>

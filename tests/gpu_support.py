@@ -22,6 +22,14 @@ ATOL = 1e-6
 SET_SLACK = 1e-4
 
 
+def floor_sample_blocks(N: int) -> np.ndarray:
+    """The blocks the prep kernel may sample to place a row's candidate floor:
+    (2j+1) N / (2S) for j < S, with S = 512 on calls of several layers and
+    S = 256 on one-layer calls.  Both sets, so that a test that gives them the
+    top scores (to force the floor too high) holds for either."""
+    return np.union1d((2 * np.arange(512) + 1) * N // 1024, (2 * np.arange(256) + 1) * N // 512)
+
+
 def run_gpu(selector: sel.Selector, p: wl.Problem, k=None):
     import torch
     q, w, keys, mask, limit = sel.upload(p)

@@ -165,14 +165,15 @@ def test_many_candidates_with_ties(selector):
 
 
 def test_rescore_when_floor_too_high(selector):
-    """The floor is placed from 512 evenly spaced blocks, (2j+1) N / 1024.  Giving exactly
-    those blocks the top scores makes the floor pass only a few dozen candidates, fewer
-    than k, so the select must rescore the whole row; the result is still exact."""
+    """The floor is placed from evenly spaced blocks, (2j+1) N / (2S) (S = 256 on this
+    one-layer call).  Giving every block either sample count can pick the top scores makes
+    the floor pass only a few dozen candidates, fewer than k, so the select must rescore
+    the whole row; the result is still exact."""
     rng = np.random.default_rng(9)
     N = 20000
     col0 = 1.0 + rng.integers(0, 128, N) / 128.0          # [1, 2): below every sampled block
-    sampled = (2 * np.arange(512) + 1) * N // 1024
-    col0[sampled] = 2.0 + rng.integers(0, 128, 512) / 64.0  # [2, 4)
+    sampled = gs.floor_sample_blocks(N)
+    col0[sampled] = 2.0 + rng.integers(0, 128, len(sampled)) / 64.0  # [2, 4)
     p = _column0_problem("rescore", col0, N)
     _print_case("rescore", p)
     gs.assert_bit_exact(gs.run_gpu(selector, p), gs.run_oracle(p), "rescore")
@@ -212,13 +213,13 @@ def test_more_rows_than_compute_units_every_select_path(selector):
     q[:, :, 0, 0] = 1.0
     w = np.ones((L, R, H), np.float32)
     keys = np.zeros((L, N, d), np.float32)
-    sampled = (2 * np.arange(512) + 1) * N // 1024
+    sampled = gs.floor_sample_blocks(N)
     for l in range(L):
         if l % 2 == 0:
             keys[l, :, 0] = 1.0 + rng.integers(0, 2, N) / 2.0
         else:
             col0 = 1.0 + rng.integers(0, 128, N) / 128.0
-            col0[sampled] = 2.0 + rng.integers(0, 128, 512) / 64.0
+            col0[sampled] = 2.0 + rng.integers(0, 128, len(sampled)) / 64.0
             keys[l, :, 0] = col0
     p = wl.Problem("many_rows_paths", k, wl.f32_to_bf16_bits(q), wl.f32_to_bf16_bits(w),
                    wl.f32_to_bf16_bits(keys), None, None, True)

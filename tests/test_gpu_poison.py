@@ -43,8 +43,8 @@ def _cases():
     rng = np.random.default_rng(9)
     N = 20000
     col0 = 1.0 + rng.integers(0, 128, N) / 128.0
-    sampled = (2 * np.arange(512) + 1) * N // 1024
-    col0[sampled] = 2.0 + rng.integers(0, 128, 512) / 64.0
+    sampled = gs.floor_sample_blocks(N)
+    col0[sampled] = 2.0 + rng.integers(0, 128, len(sampled)) / 64.0
     return [
         ("tiny", wl.make("tiny")),
         ("verify_int", wl.make("verify_int")),

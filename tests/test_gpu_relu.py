@@ -90,8 +90,8 @@ def test_relu_rescore_when_floor_too_high(selector):
     rng = np.random.default_rng(9)
     N = 20000
     col0 = 1.0 + rng.integers(0, 128, N) / 128.0
-    sampled = (2 * np.arange(512) + 1) * N // 1024
-    col0[sampled] = 2.0 + rng.integers(0, 128, 512) / 64.0
+    sampled = gs.floor_sample_blocks(N)
+    col0[sampled] = 2.0 + rng.integers(0, 128, len(sampled)) / 64.0
     p = tp._column0_problem("relu_rescore", col0, N)
     _print("rescore", p)
     gs.assert_bit_exact(gs.run_gpu(selector, p), gs.run_oracle(p, score="relu"), "relu_rescore")
