@@ -144,6 +144,7 @@ static __device__ __forceinline__ void sort_place(uint64_t* se, int n, int m, ui
 // lies inside the row's list (which has room for every position), and the
 // slots at or past c are simply never used.
 struct RegisterWords {
+  static constexpr bool kInRegisters = true;
   static constexpr int kPer = (kSelectBuf + NT - 1) / NT;
   uint64_t v[kPer];
   int c = 0;
@@ -177,6 +178,7 @@ struct RegisterWords {
 
 // Candidate words read from global memory on every pass (any count).
 struct GlobalWords {
+  static constexpr bool kInRegisters = false;
   const uint64_t* p;
   int c;
   template <class F>
@@ -209,10 +211,27 @@ static __device__ void radix_select_words(const Words& src, int c, int m, Shared
     const int shift = 64 - pbits - width;
     for (int i = tid; i < kHistBins; i += NT) sh.hist[i] = 0u;
     __syncthreads();
-    src.each([&](bool valid, uint64_t w) {
-      if (valid && (pbits == 0 || (w >> (64 - pbits)) == prefix))
-        atomicAdd(&sh.hist[(uint32_t)(w >> shift) & ((1u << width) - 1u)], 1u);
-    });
+    if constexpr (Words::kInRegisters) {
+      // The candidates all lie above the row's floor, so the first pass puts
+      // nearly all of them in a few bins, where the LDS serialises the atomics:
+      // a thread adds its words in the bin of its first one with one atomic.
+      uint32_t lead = 0u;
+      int nlead = 0;
+      src.each([&](bool valid, uint64_t w) {
+        if (valid && (pbits == 0 || (w >> (64 - pbits)) == prefix)) {
+          const uint32_t b = (uint32_t)(w >> shift) & ((1u << width) - 1u);
+          if (nlead == 0) lead = b;
+          if (nlead == 0 || b == lead) ++nlead;
+          else atomicAdd(&sh.hist[b], 1u);
+        }
+      });
+      if (nlead > 0) atomicAdd(&sh.hist[lead], (uint32_t)nlead);
+    } else {
+      src.each([&](bool valid, uint64_t w) {
+        if (valid && (pbits == 0 || (w >> (64 - pbits)) == prefix))
+          atomicAdd(&sh.hist[(uint32_t)(w >> shift) & ((1u << width) - 1u)], 1u);
+      });
+    }
     __syncthreads();
     find_boundary(sh.hist, kHistBins, need, &sh.bin, &sh.above, sh.scan);
     const int bin = sh.bin;
