@@ -227,6 +227,24 @@ def test_more_rows_than_compute_units_every_select_path(selector):
     gs.assert_bit_exact(gs.run_gpu(selector, p), gs.run_oracle(p), "many_rows_paths")
 
 
+def test_layer_alone_equals_layer_in_batch(selector):
+    """A batched call places each row's floor from 512 sampled blocks and a one-layer call
+    from 256, and their key streams cut the work into different pieces.  Neither changes
+    any key's score or the result: each layer selected alone is bit-identical to the same
+    layer inside the batch, on general (non-integer) values too."""
+    p = wl.make_custom(4, 6, 64, 128, 20000, 512, seed=330, values="normal", mask_p=0.5,
+                       limits=np.array([[20000 - 5 + r for r in range(6)]] * 4))
+    _print_case("alone_vs_batch", p)
+    batched = gs.run_gpu(selector, p)
+    for l in range(p.layers):
+        one = wl.Problem(f"{p.name}[{l}]", p.k, p.q[l:l + 1], p.w[l:l + 1], p.keys[l:l + 1],
+                         None if p.mask is None else p.mask[l:l + 1],
+                         None if p.limit is None else p.limit[l:l + 1], p.integer_valued)
+        alone = gs.run_gpu(selector, one)
+        for a, b in zip(alone, batched):
+            np.testing.assert_array_equal(a[0], b[l], err_msg=f"layer {l}")
+
+
 def test_repeated_calls_identical(selector):
     """Atomic append order must not leak into the output (tie-heavy input)."""
     import torch
